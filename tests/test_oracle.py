@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+The oracle is pinned here to things other than itself: closed forms,
+invariants, a library softmax (scipy) on the c = 1 special case, brute-force
+enumeration of chunk subsets, numpy indexing for the copy, and torch's bf16
+widening.  Each test names the mistake it is there to catch.
+
+Method: ChunkKV page, section 4.1 (Algorithm 1) and section 4.2 (Algorithm 2);
+attention probabilities: Kara page, section 2, equation (1).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import kvsynth
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+def _rand(shape, rng, dtype=np.float32):
+    return rng.standard_normal(shape).astype(dtype)
+
+
+def _chunk_lens(T, c):
+    C = -(-T // c)
+    return np.array([min(c, T - j * c) for j in range(C)], dtype=np.float64)
+
+
+# ---------------------------------------------------------------- chunking --
+
+@pytest.mark.parametrize("T,c", [(1000, 10), (8192, 10), (16384, 3), (16384, 30), (7, 3),
+                                 (1, 1), (5, 7), (32768, 10), (131072, 10)])
+def test_chunk_count_and_last_chunk(T, c):
+    # Algorithm 1 step 2: C = ceil(T_k / c), the last chunk may be short.
+    C = oracle.num_chunks(T, c)
+    assert C == math.ceil(T / c)
+    last = T - (C - 1) * c
+    assert 1 <= last <= c
+    assert _chunk_lens(T, c).sum() == T
+
+
+@pytest.mark.parametrize("l_max,c,k", [(100, 10, 10), (819, 10, 81), (3276, 10, 327),
+                                       (128, 3, 42), (512, 30, 17), (9, 10, 0)])
+def test_keep_chunk_count(l_max, c, k):
+    # Algorithm 1 step 4: k = floor(L_max / c)
+    assert oracle.num_keep_chunks(l_max, c) == k
+
+
+# ------------------------------------------------------------------ scores --
+
+@pytest.mark.parametrize("hq,hkv,d,T,w,c", [(1, 1, 64, 1000, 8, 10), (4, 2, 16, 97, 5, 7),
+                                           (8, 2, 32, 64, 64, 3), (6, 3, 8, 33, 1, 40)])
+def test_scores_sum_to_rows(hq, hkv, d, T, w, c):
+    # Invariant: every softmax row sums to one, so the chunk scores of a KV
+    # head sum to G*w.  Catches a missing or partial normalisation.
+    rng = np.random.default_rng(1)
+    q = _rand((T, hq, d), rng)
+    k = _rand((T, hkv, d), rng) * 3
+    for h in range(hkv):
+        s = oracle.chunk_scores(q, k, h, hq, w, c)
+        assert s.shape == (math.ceil(T / c),)
+        assert np.all(s > 0)
+        assert abs(s.sum() - (hq // hkv) * w) < 1e-11 * hq * w
+
+
+@pytest.mark.parametrize("zero_q", [True, False])
+def test_scores_uniform_closed_form(zero_q):
+    # Closed form: with Q = 0, or with every key equal, each row is uniform
+    # over the T keys, so S_j = G*w*len_j/T.  Catches wrong chunk bounds and
+    # an averaged (instead of summed) short last chunk.
+    rng = np.random.default_rng(2)
+    T, hq, hkv, d, w, c = 103, 4, 2, 16, 6, 10
+    q = np.zeros((T, hq, d), np.float32) if zero_q else _rand((T, hq, d), rng)
+    k = _rand((T, hkv, d), rng)
+    if not zero_q:
+        k[:] = k[0]
+    G = hq // hkv
+    expect = G * w * _chunk_lens(T, c) / T
+    for h in range(hkv):
+        np.testing.assert_allclose(oracle.chunk_scores(q, k, h, hq, w, c), expect,
+                                   rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("d", [4, 16, 64])
+def test_scores_two_level_closed_form(d):
+    # Keys are beta*e0 on a "hot" token set and 0 elsewhere; every window query
+    # is alpha*e0.  Then x = alpha*beta/sqrt(d) on hot tokens and 0 elsewhere,
+    # p_hot = e^a / Z and p_cold = 1/Z with Z = |H| e^a + T - |H|.
+    # Catches a missing 1/sqrt(d), a sign error and any causal masking.
+    T, w, c = 50, 4, 6
+    alpha, beta = 3.0, 1.5
+    hot = np.array([0, 1, 7, 13, 14, 15, 31, 49])
+    q = np.zeros((T, 1, d), np.float32)
+    q[:, 0, 0] = alpha
+    k = np.zeros((T, 1, d), np.float32)
+    k[hot, 0, 0] = beta
+    a = alpha * beta / math.sqrt(d)
+    Z = len(hot) * math.exp(a) + (T - len(hot))
+    p = np.full(T, 1.0 / Z)
+    p[hot] = math.exp(a) / Z
+    expect = np.array([w * p[j * c:(j + 1) * c].sum() for j in range(math.ceil(T / c))])
+    np.testing.assert_allclose(oracle.chunk_scores(q, k, 0, 1, w, c), expect, rtol=1e-13)
+
+
+def test_scores_gqa_grouping_closed_form():
+    # GQA: query head hq belongs to KV head hq // G.  Heads 0,1 -> KV head 0
+    # (queries along e0), heads 2,3 -> KV head 1 (queries along e1).  KV head
+    # 0 has hot tokens along e0 in chunk 1, KV head 1 hot tokens along e1 in
+    # chunk 3.  An interleaved mapping (hq % H_kv) would pair e0 queries with
+    # KV head 1 and break both closed forms.
+    T, d, w, c, hq, hkv = 40, 8, 3, 8, 4, 2
+    a_amp = 2.0
+    q = np.zeros((T, hq, d), np.float32)
+    q[:, 0:2, 0] = a_amp
+    q[:, 2:4, 1] = a_amp
+    k = np.zeros((T, hkv, d), np.float32)
+    k[8:16, 0, 0] = 1.0      # chunk 1 of head 0 along e0
+    k[24:32, 1, 1] = 1.0     # chunk 3 of head 1 along e1
+    k[0:8, 1, 0] = 1.0       # a decoy along e0 in head 1 (only e0 queries see it)
+    a = a_amp / math.sqrt(d)
+    Z = 8 * math.exp(a) + (T - 8)
+    for h, hot_chunk in ((0, 1), (1, 3)):
+        expect = np.full(5, 2 * w * 8 / Z)
+        expect[hot_chunk] = 2 * w * 8 * math.exp(a) / Z
+        np.testing.assert_allclose(oracle.chunk_scores(q, k, h, hq, w, c), expect, rtol=1e-13)
+
+
+def test_scores_read_only_the_observe_window():
+    # Algorithm 1 step 1 uses Q_{t_q-w : t_q}: rows before the window must not
+    # matter, rows inside it must.
+    rng = np.random.default_rng(3)
+    T, d, w, c = 60, 16, 5, 7
+    q = _rand((T, 2, d), rng)
+    k = _rand((T, 1, d), rng)
+    base = oracle.chunk_scores(q, k, 0, 2, w, c)
+    q2 = q.copy()
+    q2[:T - w] = 1e3 * _rand((T - w, 2, d), rng)
+    np.testing.assert_array_equal(oracle.chunk_scores(q2, k, 0, 2, w, c), base)
+    np.testing.assert_array_equal(oracle.chunk_scores(q[T - w:], k, 0, 2, w, c), base)
+    q3 = q.copy()
+    q3[T - 1, 1] += 1.0
+    assert np.abs(oracle.chunk_scores(q3, k, 0, 2, w, c) - base).max() > 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scores_c1_equal_library_softmax(dtype):
+    # Special case c = 1: S_t is the column sum of the attention probability
+    # matrix softmax(Q_w K^T / sqrt(d)) over the G*w window rows (Kara eq. 1).
+    # Checked against scipy's softmax on fp64 copies of the (exactly widened)
+    # inputs.  Catches any indexing error in the dot product or the row loop.
+    rng = np.random.default_rng(4)
+    T, hq, hkv, d, w = 37, 6, 2, 24, 4
+    qf = _rand((T, hq, d), rng)
+    kf = _rand((T, hkv, d), rng) * 2
+    if dtype == "bf16":
+        qt = torch.from_numpy(qf).to(torch.bfloat16)
+        kt = torch.from_numpy(kf).to(torch.bfloat16)
+        q, k = kvsynth.bf16_bits(qt), kvsynth.bf16_bits(kt)
+        q64, k64 = qt.double().numpy(), kt.double().numpy()
+    else:
+        q, k = qf, kf
+        q64, k64 = qf.astype(np.float64), kf.astype(np.float64)
+    G = hq // hkv
+    for h in range(hkv):
+        rows = q64[T - w:, h * G:(h + 1) * G, :].reshape(-1, d)      # (w*G, d)
+        P = scipy.special.softmax(rows @ k64[:, h, :].T / math.sqrt(d), axis=1)
+        np.testing.assert_allclose(oracle.chunk_scores(q, k, h, hq, w, 1), P.sum(axis=0),
+                                   rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("c", [2, 3, 10, 36, 37, 100])
+def test_scores_chunk_consistency_and_permutation(c):
+    # Chunk score j equals the sum of the token-level (c = 1) scores of its
+    # tokens (Algorithm 1 step 3 with bounds clamped to T), and permuting keys
+    # inside a chunk leaves it unchanged.  Catches off-by-one chunk bounds.
+    rng = np.random.default_rng(5)
+    T, d, w = 37, 8, 3
+    q = _rand((T, 2, d), rng)
+    k = _rand((T, 1, d), rng)
+    tok = oracle.chunk_scores(q, k, 0, 2, w, 1)
+    sc = oracle.chunk_scores(q, k, 0, 2, w, c)
+    expect = np.array([tok[j * c:(j + 1) * c].sum() for j in range(math.ceil(T / c))])
+    np.testing.assert_allclose(sc, expect, rtol=1e-12)
+    perm = np.arange(T)
+    for j in range(math.ceil(T / c)):
+        seg = perm[j * c:(j + 1) * c]
+        perm[j * c:(j + 1) * c] = seg[rng.permutation(seg.size)]
+    np.testing.assert_allclose(oracle.chunk_scores(q, k[perm], 0, 2, w, c), sc, rtol=1e-12)
+    if c >= T:
+        assert sc.shape == (1,) and abs(sc[0] - 2 * w) < 1e-12
+
+
+def test_bf16_inputs_widen_like_torch():
+    # bf16 bits are widened exactly: the oracle on bf16 bits equals the oracle
+    # on torch's float32 widening of the same bf16 values.  Catches a wrong
+    # bit shift or byte order in the widening.
+    rng = np.random.default_rng(6)
+    qt = torch.from_numpy(_rand((20, 2, 16), rng)).to(torch.bfloat16)
+    kt = torch.from_numpy(_rand((20, 1, 16), rng)).to(torch.bfloat16)
+    a = oracle.chunk_scores(kvsynth.bf16_bits(qt), kvsynth.bf16_bits(kt), 0, 2, 4, 3)
+    b = oracle.chunk_scores(qt.float().numpy(), kt.float().numpy(), 0, 2, 4, 3)
+    np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------------------- top-k --
+
+def _brute_topk(s, k):
+    """Max-sum k-subset; among equal sums the lexicographically smallest
+    ascending id list."""
+    C = len(s)
+    k = min(k, C)
+    best, best_ids = None, None
+    for ids in itertools.combinations(range(C), k):
+        tot = sum(s[i] for i in ids)
+        if best is None or tot > best or (tot == best and list(ids) < best_ids):
+            best, best_ids = tot, list(ids)
+    return best_ids
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_matches_brute_force(seed):
+    # Algorithm 1 step 4.  Integer-valued scores make ties common, so the
+    # lower-id-first tie rule is exercised.  Brute force enumerates subsets.
+    rng = np.random.default_rng(100 + seed)
+    C = int(rng.integers(1, 11))
+    s = rng.integers(0, 4, size=C).astype(np.float64)
+    for k in range(0, C + 3):
+        assert oracle.topk(s, k).tolist() == _brute_topk(s, k), (s, k)
+
+
+# ----------------------------------------------------------------- indices --
+
+@pytest.mark.parametrize("seed", range(10))
+def test_indices_invariants(seed):
+    # Steps 5-6: strictly increasing, every window token kept, n equals the
+    # selected chunks' tokens plus the window tokens outside them, n <= L_max + w.
+    rng = np.random.default_rng(200 + seed)
+    T = int(rng.integers(1, 200))
+    c = int(rng.integers(1, 25))
+    w = int(rng.integers(1, T + 1))
+    C = math.ceil(T / c)
+    l_max = int(rng.integers(0, T + 1))
+    kk = l_max // c
+    sel = np.sort(rng.choice(C, size=min(kk, C), replace=False)).astype(np.int32)
+    idx = oracle.indices(T, w, c, sel)
+    assert np.all(np.diff(idx) > 0)
+    assert set(range(T - w, T)) <= set(idx.tolist())
+    in_sel = {t for j in sel for t in range(j * c, min(j * c + c, T))}
+    assert set(idx.tolist()) == in_sel | set(range(T - w, T))
+    assert idx.size == len(in_sel) + len(set(range(T - w, T)) - in_sel)
+    assert idx.size <= min(T, kk * c + w) <= l_max + w
+
+
+def test_uniform_keys_select_first_chunks():
+    # Closed form: uniform keys make every full chunk tie, so the lowest ids
+    # win: indices = [0, k*c) U [T-w, T).  The short last chunk scores lower.
+    T, d, w, c, l_max = 95, 8, 7, 10, 35
+    rng = np.random.default_rng(7)
+    q = _rand((T, 1, d), rng)
+    k = np.repeat(_rand((1, 1, d), rng), T, axis=0)
+    s = oracle.chunk_scores(q, k, 0, 1, w, c)
+    idx = oracle.indices(T, w, c, oracle.topk(s, l_max // c))
+    expect = sorted(set(range(0, 3 * c)) | set(range(T - w, T)))
+    assert idx.tolist() == expect
+
+
+# ------------------------------------------------------------------ gather --
+
+@pytest.mark.parametrize("dt", [np.float32, np.uint16])
+def test_gather_is_numpy_take(dt):
+    # Step 6 index_select: row i of K' is, bit for bit, row idx[i] of head h.
+    rng = np.random.default_rng(8)
+    src = rng.integers(0, 2**16, size=(50, 3, 12)).astype(dt)
+    idx = np.sort(rng.choice(50, 17, replace=False)).astype(np.int32)
+    for h in range(3):
+        out = oracle.gather(src, idx, h)
+        np.testing.assert_array_equal(out.view(np.uint8), src[idx, h, :].view(np.uint8))
+
+
+# ---------------------------------------------------------- layer driver --
+
+@pytest.mark.parametrize("n_reuse", [1, 2, 3, 9])
+def test_compress_layers_index_reuse(n_reuse):
+    # Algorithm 2: layer l scores iff l mod N_reuse == 0; other layers reuse
+    # the index sets of layer floor(l/N_reuse)*N_reuse and gather from their
+    # OWN K/V.  Catches gathering from the anchor layer's cache.
+    rng = np.random.default_rng(9)
+    L, T, hq, hkv, d, w, c, l_max = 5, 64, 4, 2, 8, 4, 5, 20
+    qs = [_rand((T, hq, d), rng) for _ in range(L)]
+    ks = [_rand((T, hkv, d), rng) for _ in range(L)]
+    vs = [_rand((T, hkv, d), rng) for _ in range(L)]
+    qs_in = [q if l % n_reuse == 0 else None for l, q in enumerate(qs)]
+    out = oracle.compress_layers(qs_in, ks, vs, hq, w, c, l_max, n_reuse)
+    for l in range(L):
+        a = (l // n_reuse) * n_reuse
+        scored = l % n_reuse == 0
+        assert np.isfinite(out["scores"][l]).all() == scored
+        for h in range(hkv):
+            n = out["lengths"][l, h]
+            idx = out["indices"][l, h, :n]
+            if scored:
+                ref = oracle.indices(T, w, c, oracle.topk(oracle.chunk_scores(qs[l], ks[l], h, hq, w, c), l_max // c))
+                np.testing.assert_array_equal(idx, ref)
+            else:
+                np.testing.assert_array_equal(idx, out["indices"][a, h, :out["lengths"][a, h]])
+            np.testing.assert_array_equal(out["k_out"][l, h, :n], ks[l][idx, h, :])
+            np.testing.assert_array_equal(out["v_out"][l, h, :n], vs[l][idx, h, :])
+    if n_reuse > L:
+        assert np.isfinite(out["scores"][0]).all() and not np.isfinite(out["scores"][1:]).any()
+
+
+# ------------------------------------------------- the tiny planted case --
+
+def test_tiny_planted_chunks_are_selected():
+    # The 5 chunks whose keys were shifted along the window queries' mean
+    # direction raise every window row's logits on them; they should be among
+    # the k = 10 selected chunks.  n is 100 or 108 (108 unless the window's
+    # chunk 99 itself is selected).
+    d = kvsynth.make_tiny()
+    wl = kvsynth.WORKLOADS["tiny-fp32-d64-T1000"]
+    s = oracle.chunk_scores(d["q_full"], d["k"], 0, 1, wl.window, wl.chunk)
+    assert abs(s.sum() - wl.window) < 1e-10
+    sel = oracle.topk(s, oracle.num_keep_chunks(wl.l_max[0], wl.chunk))
+    assert set(d["planted"].tolist()) <= set(sel.tolist())
+    idx = oracle.indices(1000, wl.window, wl.chunk, sel)
+    assert idx.size == (100 if 99 in sel else 108)
+
+
+# ------------------------------------------------------- pages' numbers --
+
+def test_page_kv_bytes_per_token():
+    # ChunkKV page section 1: ~0.5 MB of KV per token for a 7B model, ~5 GB for
+    # a 10k-token prompt.  Pins the byte accounting used by the benchmark.
+    from kv_cache_compression_win_amd import accounting
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    m = f["kv_bytes_per_token_7b"]["model_shape"]
+    b = accounting.kv_bytes_per_token(m["n_layers"], m["n_kv_heads"], m["head_dim"], m["elem_bytes"])
+    assert b == 524288
+    assert abs(b / 2**20 - f["kv_bytes_per_token_7b"]["value_mb"]) < 1e-9
+    tot = b * f["kv_bytes_10k_prompt_7b"]["tokens"]
+    assert abs(tot / 1e9 - f["kv_bytes_10k_prompt_7b"]["value_gb"]) / 5.0 < 0.05
