@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark of ChunkKV prefill-time KV-cache compression on one MI355X.
+
+A step is one chunkkv_compress_layers call over the whole synthetic cache:
+observe-window scoring, chunk sums, top-k, recent-window merge and K/V gather
+on every layer, with layer-wise index reuse (ChunkKV page, section 4.1
+Algorithm 1 and section 4.2 Algorithm 2).  Inputs are resident in HBM before
+the timed region.
+
+Prints one JSON line: layer-tokens/s (sum over layers of the tokens
+compressed, per second), the score kernel's achieved HBM bandwidth against
+the 8 TB/s MI355X peak (phase events recorded by the library on the launch
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV tokens compressed/sec per layer·head-set + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3-8b-32layer-T32768")
+    ap.add_argument("--layers", type=int, default=None, help="use the first N layers only")
+    ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--cpu-anchor-pairs", type=int, default=2,
+                    help="oracle sample: this many (scoring, reusing) layer pairs, all KV heads")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, cache, n_pairs: int):
+    """Time the CPU oracle, as it stands, on a bounded sample: the first
+    n_pairs (anchor layer, reusing layer) pairs of sequence 0, every KV head,
+    each unit running Algorithm 1 on the anchor and the gather on both."""
+    import oracle
+    import kvsynth
+    oracle.build(force=False)
+    T = wl.seq_lens[0]
+    layers = [l for p in range(n_pairs) for l in (p * wl.n_reuse, p * wl.n_reuse + 1)
+              if l < wl.n_layers]
+    host = {l: (kvsynth.host_array(cache["k"][l, :T]), kvsynth.host_array(cache["v"][l, :T]))
+            for l in layers}
+    qh = {l: kvsynth.host_array(cache["q_win"][l, 0]) for l in layers if l % wl.n_reuse == 0}
+    kk = wl.l_max[0] // wl.chunk
+
+    def unit(args):
+        a, h = args
+        s = oracle.chunk_scores(qh[a], host[a][0], h, wl.n_q_heads, wl.window, wl.chunk)
+        idx = oracle.indices(T, wl.window, wl.chunk, oracle.topk(s, kk))
+        for l in (a, a + 1):
+            if l in host:
+                oracle.gather(host[l][0], idx, h)
+                oracle.gather(host[l][1], idx, h)
+
+    jobs = [(a, h) for a in sorted(qh) for h in range(wl.n_kv_heads)]
+    threads = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(unit, jobs))
+    dt = time.perf_counter() - t0
+    layer_tokens = len(layers) * T
+    return {"value": layer_tokens / dt, "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"layers {layers} of sequence 0 (T={T}), all {wl.n_kv_heads} KV heads: "
+                       f"fp64 scoring + full-sort top-k + index build on the scoring layers, "
+                       f"row copies on all; {dt:.2f} s wall")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: ChunkKV compression here has no multi-GPU path "
+              "(every (layer, sequence, KV head) unit is independent; see the sharding notes in "
+              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kvsynth
+    from kv_cache_compression_win_amd import accounting
+    from kv_cache_compression_win_amd import chunkkv as ck
+
+    wl = kvsynth.WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(n_layers=args.layers)
+    assert wl.dtype == "bf16"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    print(f"[bench] generating {wl.name} ({wl.n_layers} layers, T={list(wl.seq_lens)}) on {dev}",
+          file=sys.stderr, flush=True)
+    cache = kvsynth.make_cache(wl, device=dev, seed=0)
+    torch.cuda.synchronize()
+
+    L, n_reuse = wl.n_layers, wl.n_reuse
+    prob = ck.make_problem(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                           wl.window, wl.chunk)
+    bufs = ck.Buffers(prob, L, n_reuse, wl.head_dim, torch.bfloat16, dev)
+    qs = [cache["q_win"][l] if l % n_reuse == 0 else None for l in range(L)]
+    ks = [cache["k"][l] for l in range(L)]
+    vs = [cache["v"][l] for l in range(L)]
+    kos = [bufs.k_out[l] for l in range(L)]
+    vos = [bufs.v_out[l] for l in range(L)]
+
+    def step(events=None):
+        ck.compress_layers(prob, n_reuse, qs, ks, vs, kos, vos, bufs.scores, bufs.indices,
+                           bufs.lengths, bufs.workspace, bufs.ws_bytes, phase_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [ck.PhaseEvents() for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    def mean_ms(i, j):
+        return sum(e.elapsed_ms(i, j) for e in evs) / len(evs)
+
+    ph = {"score": mean_ms(0, 1), "combine": mean_ms(1, 2), "select": mean_ms(2, 3),
+          "gather": mean_ms(3, 4)}
+
+    # algorithmic bytes (kept-token counts from the actual lengths)
+    n_anchor = bufs.n_anchor
+    kept_per_anchor = bufs.lengths.view(n_anchor, -1).sum(dim=1).tolist()
+    kept_total = sum(kept_per_anchor[l // n_reuse] for l in range(L))
+    e = 2
+    k_bytes = sum(wl.seq_lens) * wl.n_kv_heads * wl.head_dim * e
+    q_bytes = len(wl.seq_lens) * wl.window * wl.n_q_heads * wl.head_dim * e
+    score_kernel_bytes = n_anchor * (k_bytes + q_bytes)
+    step_bytes = (n_anchor * accounting.score_bytes(wl.seq_lens, wl.n_q_heads, wl.n_kv_heads,
+                                                     wl.head_dim, wl.window, wl.chunk, e)
+                  + sum(accounting.select_bytes(wl.seq_lens, wl.n_kv_heads, wl.chunk, kept)
+                        for kept in kept_per_anchor)
+                  + accounting.gather_bytes(kept_total, wl.head_dim, e))
+    score_gbps = score_kernel_bytes / (ph["score"] * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    layer_tokens = L * sum(wl.seq_lens)
+    value = layer_tokens / (ms_step * 1e-3)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "layer-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_layers": L, "seq_lens": list(wl.seq_lens),
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "window": wl.window, "chunk": wl.chunk,
+                   "l_max": list(wl.l_max), "n_reuse": n_reuse, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel", "achieved": score_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": score_kernel_bytes,
+                     "avg_launch_ms": ph["score"]},
+        "step_hbm": {"achieved": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
+                     "algorithmic_bytes": step_bytes},
+        "phases_ms": ph,
+        "wall_s_timed": wall,
+    }
+    if args.cpu_baseline == "on":
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, cache, args.cpu_anchor_pairs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

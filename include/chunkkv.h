@@ -1,0 +1,209 @@
+/*
+ * chunkkv.h -- C-ABI of the MI355X (gfx950) ChunkKV prefill-time KV-cache
+ * compression library (libchunkkv.so).
+ *
+ * The method: page "ChunkKV: Semantic-Preserving KV Cache Compression for
+ * Efficient Long-Context LLM Inference" (NeurIPS'25 blog post), section 4.1,
+ * Algorithm 1 (inputs Q, K, V, observe window w, chunk size c, compressed
+ * length L_max; output K', V') and section 4.2, Algorithm 2 (layer-wise index
+ * reuse with N_reuse).  The attention probabilities are equation (1) of
+ * section 2 of the page "Kara: Efficient reasoning-LLM serving via
+ * sliding-window KV cache compression": softmax(Q K^T / sqrt(d)).
+ *
+ * What is computed, per layer l, sequence b and KV head h (T = T_b):
+ *   1. x[g,r,t] = q[g,r] . k[t] / sqrt(d) for the G = H_q/H_kv query heads of
+ *      the group (query head hq belongs to KV head hq / G) and the w window
+ *      queries r (positions T-w .. T-1), over ALL T keys, no causal mask;
+ *      p = softmax over t of each (g, r) row.
+ *   2. C = ceil(T / c) chunks; chunk j covers tokens [j*c, min(j*c+c, T)).
+ *   3. S[j] = sum over g, r and the chunk's tokens of p  (fp32).
+ *   4. the k = floor(L_max / c) chunks with the largest S are selected
+ *      (all C if k >= C, none if k == 0); equal scores: lower chunk id first.
+ *   5. the last w tokens are always kept.
+ *   6. indices = ascending, duplicate-free list of kept tokens, n of them
+ *      (n <= L_cap = min(T, k*c + w)); K'[i] = K[indices[i]], V' likewise.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned HIP device memory.  The library never
+ *     allocates, frees or keeps device memory.  Host pointers (problem
+ *     struct and the arrays it points to, pointer tables) are read during the
+ *     call only.  All buffers must stay valid until the work queued on
+ *     `stream` (a hipStream_t; NULL = default stream) has finished.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     non-OK status means nothing was launched and nothing was written;
+ *     chunkkv_last_error() then returns a message (thread-local).
+ *   - Launches are asynchronous on `stream`; there is no host<->device
+ *     synchronisation and no device-side assert.  CHUNKKV_ERR_HIP reports a
+ *     failed launch.
+ *   - Inputs (Q, K, V) are never written.  Output rows i >= n are left
+ *     untouched.
+ *   - Element offsets and strides are in elements of the problem's dtype.
+ *     Every K/V row and window-query row must start 16-byte aligned and
+ *     head_dim * elem_bytes must be a multiple of 16.
+ *   - Concurrent calls on different streams must use different workspaces
+ *     and outputs.
+ */
+#ifndef CHUNKKV_H
+#define CHUNKKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CHUNKKV_OK = 0,
+  CHUNKKV_ERR_INVALID_ARG = 1, /* a value outside the method's domain */
+  CHUNKKV_ERR_UNSUPPORTED = 2, /* valid for the method, not for this build */
+  CHUNKKV_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than planned */
+  CHUNKKV_ERR_HIP = 4          /* a HIP runtime call failed */
+} chunkkv_status;
+
+typedef enum { CHUNKKV_F32 = 0, CHUNKKV_BF16 = 1 } chunkkv_dtype;
+
+/*
+ * The problem of one layer (Algorithm 1's inputs), for a batch of
+ * independent sequences packed along the token axis.
+ *
+ * seq_start  HOST [n_seqs + 1], non-decreasing: sequence b owns key/value
+ *            token rows [seq_start[b], seq_start[b+1]); T_b = difference,
+ *            1 <= window <= T_b < 2^31.
+ * l_max      HOST [n_seqs]: L_max of each sequence, >= 0.  A budget ratio x
+ *            is passed as floor(x * T_b).
+ * K/V layout element (token row t, KV head h, dim i) at
+ *            t*kv_stride_tok + h*kv_stride_head + i.
+ * Window queries: element (sequence b, window row r, query head hq, dim i)
+ *            at b*q_stride_seq + r*q_stride_row + hq*q_stride_head + i; row r
+ *            is the query at position T_b - w + r (Algorithm 1 step 1 reads
+ *            only these w rows).
+ */
+typedef struct {
+  int32_t dtype;             /* chunkkv_dtype; Q, K, V, K', V' share it */
+  int32_t n_seqs;            /* B >= 1 */
+  const int64_t *seq_start;  /* HOST [B + 1] */
+  const int64_t *l_max;      /* HOST [B] */
+  int32_t n_q_heads;         /* H_q >= 1, multiple of n_kv_heads */
+  int32_t n_kv_heads;        /* H_kv >= 1 */
+  int32_t head_dim;          /* d: 8..256, d * elem_bytes multiple of 16 */
+  int32_t window;            /* w >= 1 */
+  int32_t chunk;             /* c >= 1 */
+  int32_t reserved;          /* must be 0 */
+  int64_t kv_stride_tok, kv_stride_head;
+  int64_t q_stride_seq, q_stride_row, q_stride_head;
+} chunkkv_problem;
+
+/*
+ * Sizes of one layer's outputs.  "Per scoring layer" buffers (scores,
+ * indices, lengths) hold one block per layer that runs selection; K'/V' are
+ * per layer.
+ *   scores : fp32, element (b, h, j) at score_off[b] + h*C_b + j
+ *   indices: int32, element (b, h, i) at index_off[b] + h*L_cap_b + i
+ *   lengths: int32, element (b, h) at b*H_kv + h  (= n of that head)
+ *   K', V' : rows of head_dim elements; row (b, h, i) is row
+ *            index_off[b] + h*L_cap_b + i, i.e. head-major and position
+ *            ordered per sequence.
+ */
+typedef struct {
+  int64_t scores_elems;      /* sum_b H_kv * C_b */
+  int64_t index_elems;       /* sum_b H_kv * L_cap_b (also the K'/V' row count) */
+  int64_t length_elems;      /* B * H_kv */
+  size_t workspace_bytes;    /* workspace for chunkkv_score on one layer */
+} chunkkv_sizes;
+
+/* Number of phase events chunkkv_compress_layers can record. */
+#define CHUNKKV_N_PHASE_EVENTS 5
+
+/*
+ * Host-only planning: validates the problem and fills the sizes and, when
+ * the arrays are non-NULL, the per-sequence offsets (HOST arrays of n_seqs
+ * entries) and L_cap_b = min(T_b, floor(L_max_b / c) * c + w).  Touches no
+ * device and needs no GPU.
+ * Errors: CHUNKKV_ERR_INVALID_ARG / CHUNKKV_ERR_UNSUPPORTED, nothing written.
+ */
+int chunkkv_plan(const chunkkv_problem *p, chunkkv_sizes *out, int64_t *score_off,
+                 int64_t *index_off, int64_t *l_cap);
+
+/*
+ * Workspace needed by chunkkv_compress_layers to score `n_score_layers`
+ * layers per launch (1 <= n_score_layers; more layers per launch means fewer
+ * launches).  Host only.  Returns 0 on invalid input.
+ */
+size_t chunkkv_workspace_bytes(const chunkkv_problem *p, int32_t n_score_layers);
+
+/*
+ * Algorithm 1 steps 1-3 (ChunkKV page, section 4.1) with Kara eq. (1):
+ * observe-window attention of every (sequence, KV head), summed into the
+ * C_b chunk scores.
+ *   q_win     DEVICE window queries (layout in chunkkv_problem)
+ *   k         DEVICE keys (layout in chunkkv_problem)
+ *   scores    DEVICE fp32 out, scores_elems entries (layout: chunkkv_sizes)
+ *   workspace DEVICE scratch of >= chunkkv_sizes.workspace_bytes bytes
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (ws NULL or too small), HIP.
+ */
+int chunkkv_score(const chunkkv_problem *p, const void *q_win, const void *k, float *scores,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Algorithm 1 steps 4-6 (ChunkKV page, section 4.1; the TopK -> index form
+ * is Kara eqs. (2)-(3)): per (sequence, KV head) select the floor(L_max/c)
+ * top-scoring chunks (ties: lower chunk id), add the last w tokens, and write
+ * the kept token positions (0-based within the sequence) in ascending order.
+ *   scores   DEVICE fp32, as written by chunkkv_score (scores must be >= 0 and
+ *            finite)
+ *   indices  DEVICE int32 out, index_elems entries (entries i >= n untouched)
+ *   lengths  DEVICE int32 out, length_elems entries
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int chunkkv_select(const chunkkv_problem *p, const float *scores, int32_t *indices,
+                   int32_t *lengths, void *stream);
+
+/*
+ * Algorithm 1 step 6, index_select (ChunkKV page, section 4.1): byte copy of
+ * the kept K and V rows into the compacted caches.
+ *   k, v          DEVICE inputs (layout in chunkkv_problem)
+ *   indices, lengths  DEVICE, as written by chunkkv_select (any layer's)
+ *   k_out, v_out  DEVICE out, index_elems rows of head_dim elements each
+ *                 (16-byte aligned); rows i >= n untouched
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Index values are trusted: each must
+ * lie in [0, T_b).
+ */
+int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
+                   const int32_t *indices, const int32_t *lengths, void *k_out, void *v_out,
+                   void *stream);
+
+/*
+ * Algorithm 2 (ChunkKV page, section 4.2, layer-wise index reuse) over
+ * n_layers layers sharing one problem shape: layer l scores and selects iff
+ * l mod n_reuse == 0 (an anchor layer); every other layer gathers its OWN
+ * K/V with the indices of anchor floor(l / n_reuse) * n_reuse.
+ *   q_win, k, v     HOST tables [n_layers] of DEVICE pointers (q_win[l] may be
+ *                   NULL where l mod n_reuse != 0)
+ *   k_out, v_out    HOST tables [n_layers] of DEVICE outputs
+ *   scores, indices, lengths  DEVICE, n_anchor = ceil(n_layers / n_reuse)
+ *                   consecutive per-scoring-layer blocks (block a belongs to
+ *                   layer a * n_reuse)
+ *   workspace       DEVICE scratch of >= chunkkv_workspace_bytes(p, 1) bytes;
+ *                   a larger one lets more anchor layers share a launch
+ *   phase_events    NULL, or HOST [CHUNKKV_N_PHASE_EVENTS] hipEvent_t handles
+ *                   recorded on `stream` before the score kernels, after
+ *                   them, after the score-combine kernels, after selection
+ *                   and after the gathers (for timing; any entry may be NULL)
+ * Errors: INVALID_ARG (incl. n_layers < 1, n_reuse < 1, a NULL table entry
+ * that is needed), UNSUPPORTED, WORKSPACE, HIP.
+ */
+int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t n_reuse,
+                            const void *const *q_win, const void *const *k,
+                            const void *const *v, void *const *k_out, void *const *v_out,
+                            float *scores, int32_t *indices, int32_t *lengths, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *phase_events);
+
+/* Message of this thread's last non-OK status ("" if none). */
+const char *chunkkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKKV_H */

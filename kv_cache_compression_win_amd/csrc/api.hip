@@ -1,0 +1,490 @@
+// Host side of libchunkkv.so: validation, planning and launch sequencing
+// behind the C-ABI declared in include/chunkkv.h.
+//
+// Phases (ChunkKV page, section 4.1 Algorithm 1 and section 4.2 Algorithm 2):
+//   score    window attention -> per-row chunk partials   (score_mfma / score_generic)
+//   combine  log-sum-exp normalisation -> chunk scores      (combine)
+//   select   top-k chunks + recent window -> indices        (select)
+//   gather   index_select of K and V                        (gather)
+// Everything is validated here before the first launch; launches are
+// asynchronous on the caller's stream and nothing synchronises with the host.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "chunkkv.h"
+#include "chunkkv_internal.h"
+
+namespace {
+
+using namespace ckv;
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return CHUNKKV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(CHUNKKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Seq {
+  int64_t tok0;
+  int32_t T, C, kk, L_cap, n_span;
+  int64_t score_off, index_off, u_off, st_off;
+};
+
+struct Plan {
+  int dtype = 0, eb = 0, B = 0, Hq = 0, Hkv = 0, G = 0, d = 0, w = 0, c = 0;
+  int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
+  bool mfma = false;
+  std::vector<Seq> seq;
+  int64_t scores_elems = 0, index_elems = 0, length_elems = 0, u_elems = 0, st_elems = 0;
+  int64_t kv_st = 0, kv_sh = 0, q_ss = 0, q_sr = 0, q_sh = 0;
+  size_t ws_bytes(int n_layers) const {
+    return align_up(static_cast<size_t>(n_layers) * u_elems * sizeof(float)) +
+           align_up(static_cast<size_t>(n_layers) * st_elems * sizeof(float2));
+  }
+};
+
+int make_plan(const chunkkv_problem* p, Plan& pl) {
+  if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
+  if (p->reserved != 0) return fail(CHUNKKV_ERR_INVALID_ARG, "reserved field must be 0");
+  if (p->dtype != CHUNKKV_F32 && p->dtype != CHUNKKV_BF16)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "dtype %d is neither CHUNKKV_F32 nor CHUNKKV_BF16", p->dtype);
+  if (p->n_seqs < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", p->n_seqs);
+  if (!p->seq_start || !p->l_max) return fail(CHUNKKV_ERR_INVALID_ARG, "seq_start and l_max must be non-NULL");
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->window < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "window must be >= 1 (got %d)", p->window);
+  if (p->chunk < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", p->chunk);
+  if (p->head_dim < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "head_dim must be >= 1");
+  const int eb = p->dtype == CHUNKKV_F32 ? 4 : 2;
+  if (p->head_dim < 8 || p->head_dim > 256 || (p->head_dim * eb) % 16 != 0)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "head_dim %d unsupported (8..256, rows a multiple of 16 bytes)",
+                p->head_dim);
+  if (p->kv_stride_tok < 1 || p->kv_stride_head < 0 || p->q_stride_seq < 0 || p->q_stride_row < 0 ||
+      p->q_stride_head < 0)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "strides must be non-negative (kv_stride_tok >= 1)");
+  if ((p->kv_stride_tok * eb) % 16 || (p->kv_stride_head * eb) % 16 || (p->q_stride_seq * eb) % 16 ||
+      (p->q_stride_row * eb) % 16 || (p->q_stride_head * eb) % 16)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "strides must keep every row 16-byte aligned");
+  const int64_t R = static_cast<int64_t>(p->n_q_heads / p->n_kv_heads) * p->window;
+  if (R > 4096) return fail(CHUNKKV_ERR_UNSUPPORTED, "G*w = %lld window rows per KV head exceeds 4096",
+                            static_cast<long long>(R));
+  if (p->seq_start[0] < 0) return fail(CHUNKKV_ERR_INVALID_ARG, "seq_start[0] must be >= 0");
+
+  pl = Plan{};
+  pl.dtype = p->dtype;
+  pl.eb = eb;
+  pl.B = p->n_seqs;
+  pl.Hq = p->n_q_heads;
+  pl.Hkv = p->n_kv_heads;
+  pl.G = p->n_q_heads / p->n_kv_heads;
+  pl.d = p->head_dim;
+  pl.w = p->window;
+  pl.c = p->chunk;
+  pl.R = static_cast<int>(R);
+  pl.mfma = p->dtype == CHUNKKV_BF16 && p->head_dim == 128 && score_mfma_supported(p->chunk);
+  pl.R_pad = static_cast<int>(pl.mfma ? round_up(R, kMfmaRows) : round_up(R, 4));
+  pl.n_rb = pl.mfma ? pl.R_pad / kMfmaRows : 1;
+  pl.span_chunks = pl.mfma ? score_mfma_span_chunks(pl.c) : score_generic_span_chunks(pl.R_pad, pl.c);
+  pl.kv_st = p->kv_stride_tok;
+  pl.kv_sh = p->kv_stride_head;
+  pl.q_ss = p->q_stride_seq;
+  pl.q_sr = p->q_stride_row;
+  pl.q_sh = p->q_stride_head;
+
+  int64_t items = 0;
+  for (int b = 0; b < pl.B; ++b) {
+    const int64_t T = p->seq_start[b + 1] - p->seq_start[b];
+    if (T < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "sequence %d is empty or seq_start decreases", b);
+    if (T < p->window)
+      return fail(CHUNKKV_ERR_INVALID_ARG, "window %d exceeds sequence %d length %lld", p->window, b,
+                  static_cast<long long>(T));
+    if (T > 2147483647LL - p->chunk - 64)
+      return fail(CHUNKKV_ERR_UNSUPPORTED, "sequence %d longer than 2^31 tokens", b);
+    if (p->l_max[b] < 0) return fail(CHUNKKV_ERR_INVALID_ARG, "l_max[%d] must be >= 0", b);
+    Seq s{};
+    s.tok0 = p->seq_start[b];
+    s.T = static_cast<int32_t>(T);
+    s.C = static_cast<int32_t>((T + pl.c - 1) / pl.c);
+    s.kk = static_cast<int32_t>(std::min<int64_t>(p->l_max[b] / pl.c, s.C));
+    s.L_cap = static_cast<int32_t>(std::min<int64_t>(T, static_cast<int64_t>(s.kk) * pl.c + pl.w));
+    s.n_span = (s.C + pl.span_chunks - 1) / pl.span_chunks;
+    s.score_off = pl.scores_elems;
+    s.index_off = pl.index_elems;
+    s.u_off = pl.u_elems;
+    s.st_off = pl.st_elems;
+    pl.scores_elems += static_cast<int64_t>(pl.Hkv) * s.C;
+    pl.index_elems += static_cast<int64_t>(pl.Hkv) * s.L_cap;
+    pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * pl.R_pad;
+    pl.st_elems += static_cast<int64_t>(pl.Hkv) * s.n_span * pl.R_pad;
+    items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * s.n_span;
+    pl.seq.push_back(s);
+  }
+  if (items * kMaxLayers > 2000000000LL)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  pl.length_elems = static_cast<int64_t>(pl.B) * pl.Hkv;
+  return CHUNKKV_OK;
+}
+
+// ------------------------------------------------------------- launchers --
+
+hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U,
+                     float2* st, hipStream_t s) {
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    ScoreParams P{};
+    for (int i = 0; i < nl; ++i) {
+      P.q[i] = q[i];
+      P.k[i] = k[i];
+    }
+    P.n_layers = nl;
+    P.n_seqs = nb;
+    P.span_chunks = pl.span_chunks;
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.tok0[i] = sq.tok0;
+      P.qseq[i] = b0 + i;
+      P.T[i] = sq.T;
+      P.C[i] = sq.C;
+      P.n_span[i] = sq.n_span;
+      P.item0[i] = items;
+      P.u_off[i] = sq.u_off;
+      P.st_off[i] = sq.st_off;
+      items += pl.Hkv * pl.n_rb * sq.n_span;
+    }
+    P.item0[nb] = items;
+    P.items_per_layer = items;
+    P.u_layer_stride = pl.u_elems;
+    P.st_layer_stride = pl.st_elems;
+    P.U = U;
+    P.stats = st;
+    P.H_q = pl.Hq;
+    P.H_kv = pl.Hkv;
+    P.G = pl.G;
+    P.w = pl.w;
+    P.c = pl.c;
+    P.d = pl.d;
+    P.R = pl.R;
+    P.R_pad = pl.R_pad;
+    P.n_rb = pl.n_rb;
+    P.kv_st = pl.kv_st;
+    P.kv_sh = pl.kv_sh;
+    P.q_ss = pl.q_ss;
+    P.q_sr = pl.q_sr;
+    P.q_sh = pl.q_sh;
+    P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
+    P.rebase_raw = kRebaseLog2 / P.scale;
+    const int nblk = nl * items;
+    const hipError_t e = pl.mfma ? launch_score_mfma(P, nblk, s) : launch_score_generic(P, pl.dtype, nblk, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float* scores,
+                       hipStream_t s) {
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    CombineParams P{};
+    P.n_layers = nl;
+    P.n_seqs = nb;
+    P.span_chunks = pl.span_chunks;
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.C[i] = sq.C;
+      P.n_span[i] = sq.n_span;
+      P.item0[i] = items;
+      P.u_off[i] = sq.u_off;
+      P.st_off[i] = sq.st_off;
+      P.score_off[i] = sq.score_off;
+      items += pl.Hkv * sq.n_span;
+    }
+    P.item0[nb] = items;
+    P.items_per_layer = items;
+    P.u_layer_stride = pl.u_elems;
+    P.st_layer_stride = pl.st_elems;
+    P.score_layer_stride = pl.scores_elems;
+    P.U = U;
+    P.stats = st;
+    P.scores = scores;
+    P.H_kv = pl.Hkv;
+    P.R = pl.R;
+    P.R_pad = pl.R_pad;
+    P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
+    const hipError_t e = launch_combine(P, nl * items, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_select(const Plan& pl, int nl, const float* scores, int32_t* indices, int32_t* lengths,
+                      hipStream_t s) {
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    SelectParams P{};
+    P.n_layers = nl;
+    P.n_seqs = nb;
+    P.H_kv = pl.Hkv;
+    P.w = pl.w;
+    P.c = pl.c;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.T[i] = sq.T;
+      P.C[i] = sq.C;
+      P.kk[i] = sq.kk;
+      P.L_cap[i] = sq.L_cap;
+      P.len_off[i] = (b0 + i) * pl.Hkv;
+      P.score_off[i] = sq.score_off;
+      P.index_off[i] = sq.index_off;
+    }
+    P.score_layer_stride = pl.scores_elems;
+    P.index_layer_stride = pl.index_elems;
+    P.len_layer_stride = pl.length_elems;
+    P.scores = scores;
+    P.indices = indices;
+    P.lengths = lengths;
+    const hipError_t e = launch_select(P, nl * nb * pl.Hkv, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Gathers layers [l0, l0 + nl); layer l reads index block blocks[l - l0].
+hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* const* v,
+                      void* const* ko, void* const* vo, const int32_t* blocks, const int32_t* indices,
+                      const int32_t* lengths, hipStream_t s) {
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    GatherParams P{};
+    for (int i = 0; i < nl; ++i) {
+      P.k[i] = k[i];
+      P.v[i] = v[i];
+      P.ko[i] = ko[i];
+      P.vo[i] = vo[i];
+      P.idx_block[i] = blocks[i];
+    }
+    P.n_layers = nl;
+    P.n_seqs = nb;
+    P.H_kv = pl.Hkv;
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.tok0[i] = sq.tok0;
+      P.L_cap[i] = sq.L_cap;
+      P.len_off[i] = (b0 + i) * pl.Hkv;
+      P.item0[i] = items;
+      P.blocks_per_head[i] = (sq.L_cap + kGatherRows - 1) / kGatherRows;
+      P.index_off[i] = sq.index_off;
+      items += pl.Hkv * P.blocks_per_head[i];
+    }
+    P.item0[nb] = items;
+    P.items_per_layer = items;
+    P.index_layer_stride = pl.index_elems;
+    P.len_layer_stride = pl.length_elems;
+    P.indices = indices;
+    P.lengths = lengths;
+    P.row_bytes = pl.d * pl.eb;
+    P.kv_st_bytes = pl.kv_st * pl.eb;
+    P.kv_sh_bytes = pl.kv_sh * pl.eb;
+    const hipError_t e = launch_gather(P, nl * items, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+void carve(const Plan& pl, int nl, void* ws, float** U, float2** st) {
+  *U = static_cast<float*>(ws);
+  *st = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                  align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float)));
+}
+
+int check_ws(const Plan& pl, const void* ws, size_t ws_bytes, int nl) {
+  if (!ws) return fail(CHUNKKV_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(CHUNKKV_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  const size_t need = pl.ws_bytes(nl);
+  if (ws_bytes < need)
+    return fail(CHUNKKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return CHUNKKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int chunkkv_plan(const chunkkv_problem* p, chunkkv_sizes* out, int64_t* score_off, int64_t* index_off,
+                 int64_t* l_cap) {
+  Plan pl;
+  const int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!out) return fail(CHUNKKV_ERR_INVALID_ARG, "sizes output is NULL");
+  out->scores_elems = pl.scores_elems;
+  out->index_elems = pl.index_elems;
+  out->length_elems = pl.length_elems;
+  out->workspace_bytes = pl.ws_bytes(1);
+  for (int b = 0; b < pl.B; ++b) {
+    if (score_off) score_off[b] = pl.seq[b].score_off;
+    if (index_off) index_off[b] = pl.seq[b].index_off;
+    if (l_cap) l_cap[b] = pl.seq[b].L_cap;
+  }
+  return ok();
+}
+
+size_t chunkkv_workspace_bytes(const chunkkv_problem* p, int32_t n_score_layers) {
+  Plan pl;
+  if (make_plan(p, pl) || n_score_layers < 1) return 0;
+  return pl.ws_bytes(std::min<int32_t>(n_score_layers, kMaxLayers));
+}
+
+int chunkkv_score(const chunkkv_problem* p, const void* q_win, const void* k, float* scores, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!q_win || !k || !scores) return fail(CHUNKKV_ERR_INVALID_ARG, "q_win, k and scores must be non-NULL");
+  if (!aligned16(q_win) || !aligned16(k) || reinterpret_cast<uintptr_t>(scores) % 4)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "q_win and k must be 16-byte aligned");
+  if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* U;
+  float2* st;
+  carve(pl, 1, workspace, &U, &st);
+  hipError_t e = run_score(pl, 1, &q_win, &k, U, st, s);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  e = run_combine(pl, 1, U, st, scores, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+int chunkkv_select(const chunkkv_problem* p, const float* scores, int32_t* indices, int32_t* lengths,
+                   void* stream) {
+  Plan pl;
+  const int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!scores || !indices || !lengths)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "scores, indices and lengths must be non-NULL");
+  const hipError_t e = run_select(pl, 1, scores, indices, lengths, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+int chunkkv_gather(const chunkkv_problem* p, const void* k, const void* v, const int32_t* indices,
+                   const int32_t* lengths, void* k_out, void* v_out, void* stream) {
+  Plan pl;
+  const int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!k || !v || !indices || !lengths || !k_out || !v_out)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "k, v, indices, lengths, k_out and v_out must be non-NULL");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "K/V buffers must be 16-byte aligned");
+  const int32_t blk = 0;
+  const hipError_t e = run_gather(pl, 1, &k, &v, &k_out, &v_out, &blk, indices, lengths,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t n_reuse,
+                            const void* const* q_win, const void* const* k, const void* const* v,
+                            void* const* k_out, void* const* v_out, float* scores, int32_t* indices,
+                            int32_t* lengths, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* phase_events) {
+  Plan pl;
+  int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (n_layers < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "n_layers must be >= 1 (got %d)", n_layers);
+  if (n_reuse < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "n_reuse must be >= 1 (got %d)", n_reuse);
+  if (!q_win || !k || !v || !k_out || !v_out)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "pointer tables must be non-NULL");
+  if (!scores || !indices || !lengths)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "scores, indices and lengths must be non-NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if (l % n_reuse == 0 && !q_win[l])
+      return fail(CHUNKKV_ERR_INVALID_ARG, "q_win[%d] is NULL on a scoring layer", l);
+    if (!k[l] || !v[l] || !k_out[l] || !v_out[l])
+      return fail(CHUNKKV_ERR_INVALID_ARG, "a K/V pointer of layer %d is NULL", l);
+    if ((l % n_reuse == 0 && !aligned16(q_win[l])) || !aligned16(k[l]) || !aligned16(v[l]) ||
+        !aligned16(k_out[l]) || !aligned16(v_out[l]))
+      return fail(CHUNKKV_ERR_UNSUPPORTED, "buffers of layer %d must be 16-byte aligned", l);
+  }
+  const int n_anchor = (n_layers + n_reuse - 1) / n_reuse;
+  if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
+  int batch = std::min(n_anchor, kMaxLayers);
+  while (batch > 1 && pl.ws_bytes(batch) > workspace_bytes) --batch;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto record = [&](int i) -> hipError_t {
+    if (phase_events && phase_events[i])
+      return hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s);
+    return hipSuccess;
+  };
+  hipError_t e = record(0);
+  if (e != hipSuccess) return hip_fail(e, "phase event");
+
+  float* U;
+  float2* st;
+  carve(pl, batch, workspace, &U, &st);
+  const bool one_batch = n_anchor <= batch;
+  const void* qb[kMaxLayers];
+  const void* kb[kMaxLayers];
+  for (int a0 = 0; a0 < n_anchor; a0 += batch) {
+    const int na = std::min(batch, n_anchor - a0);
+    for (int i = 0; i < na; ++i) {
+      qb[i] = q_win[(a0 + i) * n_reuse];
+      kb[i] = k[(a0 + i) * n_reuse];
+    }
+    if ((e = run_score(pl, na, qb, kb, U, st, s)) != hipSuccess) return hip_fail(e, "score launch");
+    if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
+    if ((e = run_combine(pl, na, U, st, scores + a0 * pl.scores_elems, s)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+  }
+  if (!one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
+  if ((e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
+
+  if ((e = run_select(pl, n_anchor, scores, indices, lengths, s)) != hipSuccess)
+    return hip_fail(e, "select launch");
+  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+
+  int32_t blocks[kMaxLayers];
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, n_layers - l0);
+    for (int i = 0; i < nl; ++i) blocks[i] = (l0 + i) / n_reuse;
+    if ((e = run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s)) !=
+        hipSuccess)
+      return hip_fail(e, "gather launch");
+  }
+  if ((e = record(4)) != hipSuccess) return hip_fail(e, "phase event");
+  return ok();
+}
+
+const char* chunkkv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

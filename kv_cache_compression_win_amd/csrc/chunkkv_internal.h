@@ -1,0 +1,137 @@
+// Internal definitions shared by the HIP kernels and the host side of
+// libchunkkv.so (gfx950 / CDNA4).  Not part of the C-ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckv {
+
+// Per-launch table limits: layer pointers and per-sequence geometry travel in
+// kernel arguments; the host splits larger problems into several launches.
+constexpr int kMaxLayers = 32;
+constexpr int kMaxSeqs = 8;
+
+constexpr int kThreads = 256;            // every kernel: 4 wave64s per workgroup
+constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score workgroup
+constexpr int kGatherRows = 64;          // output rows per gather workgroup
+
+// A chunk-partial reference is rebased only when a new maximum exceeds the
+// current reference by this many powers of two; below that, exp2 of the
+// difference stays far inside fp32 range (2^64 * tokens << FLT_MAX).
+constexpr float kRebaseLog2 = 64.0f;
+
+// ----------------------------------------------------------------- score --
+// One launch scores up to kMaxLayers layers x kMaxSeqs sequences.  Work item
+// = (layer, sequence b, KV head h, row block rb, span s); a span is a run of
+// span_chunks whole chunks.  Each item writes
+//   U[layer][u_off[b] + (h*C_b + j)*R_pad + r]      chunk partials
+//   stats[layer][st_off[b] + (h*n_span_b + s)*R_pad + r] = (m_ref, l)
+// where U is sum over the chunk's tokens of exp2((x - m_ref)*scale) and l
+// is sum over the span of the same terms.
+struct ScoreParams {
+  const void* q[kMaxLayers];
+  const void* k[kMaxLayers];
+  int32_t n_layers;
+  int32_t n_seqs;
+  int32_t items_per_layer;
+  int32_t span_chunks;
+  int64_t tok0[kMaxSeqs];       // first K/V token row of sequence b
+  int32_t qseq[kMaxSeqs];       // sequence index for q_stride_seq
+  int32_t T[kMaxSeqs];
+  int32_t C[kMaxSeqs];
+  int32_t n_span[kMaxSeqs];
+  int32_t item0[kMaxSeqs + 1];  // first item of sequence b within a layer
+  int64_t u_off[kMaxSeqs];
+  int64_t st_off[kMaxSeqs];
+  int64_t u_layer_stride;
+  int64_t st_layer_stride;
+  float* U;
+  float2* stats;
+  int32_t H_q, H_kv, G, w, c, d, R, R_pad, n_rb;
+  int64_t kv_st, kv_sh, q_ss, q_sr, q_sh;
+  float scale;                  // log2(e) / sqrt(d)
+  float rebase_raw;             // kRebaseLog2 / scale
+};
+
+// --------------------------------------------------------------- combine --
+// Item = (layer, b, h, span): S_j = sum_r U[j][r] * 2^((m_s,r - M_r)*scale) / L_r
+// with M_r, L_r the row's log-sum-exp over all spans of the head.
+struct CombineParams {
+  int32_t n_layers;
+  int32_t n_seqs;
+  int32_t items_per_layer;
+  int32_t span_chunks;
+  int32_t C[kMaxSeqs];
+  int32_t n_span[kMaxSeqs];
+  int32_t item0[kMaxSeqs + 1];
+  int64_t u_off[kMaxSeqs];
+  int64_t st_off[kMaxSeqs];
+  int64_t score_off[kMaxSeqs];
+  int64_t u_layer_stride, st_layer_stride, score_layer_stride;
+  const float* U;
+  const float2* stats;
+  float* scores;
+  int32_t H_kv, R, R_pad;
+  float scale;
+};
+
+// ---------------------------------------------------------------- select --
+// Item = (scoring layer, b, h).  Radix top-k over fp32 score bit patterns,
+// recent-window merge, ascending index list.
+struct SelectParams {
+  int32_t n_layers;
+  int32_t n_seqs;
+  int32_t H_kv, w, c;
+  int32_t T[kMaxSeqs];
+  int32_t C[kMaxSeqs];
+  int32_t kk[kMaxSeqs];         // floor(L_max / c)
+  int32_t L_cap[kMaxSeqs];
+  int32_t len_off[kMaxSeqs];    // b_global * H_kv
+  int64_t score_off[kMaxSeqs];
+  int64_t index_off[kMaxSeqs];
+  int64_t score_layer_stride, index_layer_stride, len_layer_stride;
+  const float* scores;
+  int32_t* indices;
+  int32_t* lengths;
+};
+
+// ---------------------------------------------------------------- gather --
+// Item = (layer, b, h, block of kGatherRows output rows).
+struct GatherParams {
+  const void* k[kMaxLayers];
+  const void* v[kMaxLayers];
+  void* ko[kMaxLayers];
+  void* vo[kMaxLayers];
+  int32_t idx_block[kMaxLayers];  // scoring-layer block of indices/lengths
+  int32_t n_layers;
+  int32_t n_seqs;
+  int32_t H_kv;
+  int32_t items_per_layer;
+  int64_t tok0[kMaxSeqs];
+  int32_t L_cap[kMaxSeqs];
+  int32_t len_off[kMaxSeqs];
+  int32_t item0[kMaxSeqs + 1];
+  int32_t blocks_per_head[kMaxSeqs];
+  int64_t index_off[kMaxSeqs];
+  int64_t index_layer_stride, len_layer_stride;
+  const int32_t* indices;
+  const int32_t* lengths;
+  int32_t row_bytes;            // head_dim * elem_bytes, multiple of 16
+  int64_t kv_st_bytes, kv_sh_bytes;
+};
+
+// Host-side launchers (defined next to their kernels).
+// MFMA path: bf16, head_dim 128, chunk size with a static layout.
+bool score_mfma_supported(int chunk);
+int score_mfma_span_chunks(int chunk);
+hipError_t launch_score_mfma(const ScoreParams& p, int n_blocks, hipStream_t s);
+// Generic path: any dtype / head_dim / chunk size (VALU fp32).
+int score_generic_span_chunks(int R_pad, int chunk);
+size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d);
+hipError_t launch_score_generic(const ScoreParams& p, int dtype, int n_blocks, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s);
+
+}  // namespace ckv

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Method: ChunkKV page, section 4.1 (Algorithm 1) and 4.2 (Algorithm 2);
+softmax(QK^T/sqrt(d)) from Kara eq. (1).  Tolerances and the selection band
+rule are in tests/harness.py.  Small cases are checked on every unit; the
+workload-sized cases (the 8k layer, the 32-layer 32k stack that the benchmark
+times, the chunk-size sweep and the 70B-shaped batch) check sampled units
+against the oracle and properties on all units.
+"""
+import concurrent.futures
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle
+from harness import (ATOL, POISON_INDEX, RTOL, Case, check_gather, check_scores, check_selection,
+                     check_unit, random_case)
+from kv_cache_compression_win_amd import chunkkv as ck
+
+pytestmark = pytest.mark.gpu
+
+POOL = concurrent.futures.ThreadPoolExecutor(max_workers=8)
+
+
+def _all_units(case, layers=None):
+    layers = range(case.L) if layers is None else layers
+    anchors = sorted({(l // case.n_reuse) * case.n_reuse for l in layers})
+    jobs = {}
+    for a in anchors:
+        for b in range(len(case.seq_lens)):
+            for h in range(case.Hkv):
+                jobs[(a, b, h)] = POOL.submit(oracle.chunk_scores, case.host_q(a, b),
+                                              case.host_kv(case.k, a, b), h, case.Hq, case.w, case.c)
+    for l in layers:
+        a = (l // case.n_reuse) * case.n_reuse
+        for b in range(len(case.seq_lens)):
+            for h in range(case.Hkv):
+                check_unit(case, l, b, h, s_ref=jobs[(a, b, h)].result())
+
+
+# ------------------------------------------------------------ small shapes --
+
+def test_tiny_fp32_workload():
+    # 1 layer, 1 KV head, 1 query head, d=64, T=1000, fp32, 5 planted chunks;
+    # w=8, c=10, L_max=100.  Generic (VALU) score path.
+    d = kvsynth.make_tiny()
+    wl = kvsynth.WORKLOADS["tiny-fp32-d64-T1000"]
+    q = torch.from_numpy(d["q_full"][-wl.window:]).cuda()[None, None]     # [1,1,w,1,64]
+    k = torch.from_numpy(d["k"]).cuda()[None]
+    v = torch.from_numpy(d["v"]).cuda()[None]
+    case = Case(ck.F32, wl.seq_lens, wl.l_max, 1, 1, 64, wl.window, wl.chunk, 1, q, k, v).run()
+    check_unit(case, 0, 0, 0)
+    sel = oracle.topk(case.gpu_scores(0, 0, 0).astype(np.float64), 10)
+    assert set(d["planted"].tolist()) <= set(sel.tolist())
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 5, 8, 10, 16, 20, 30, 32, 64])
+def test_bf16_mfma_chunk_sizes(c):
+    # MFMA path for every statically laid-out chunk size: several spans and
+    # groups per head, a ragged last span and a short last chunk.
+    T = 1737
+    case = random_case(ck.BF16, [T], [T // 7], 8, 2, 128, 32, c, seed=c).run()
+    _all_units(case)
+
+
+@pytest.mark.parametrize("dtype,d,c,Hq,Hkv,w", [
+    (ck.F32, 128, 10, 8, 2, 16),     # fp32 inputs
+    (ck.BF16, 64, 10, 8, 2, 16),     # head_dim without an MFMA path
+    (ck.BF16, 128, 7, 4, 1, 32),     # chunk size without a static layout
+    (ck.BF16, 128, 100, 4, 2, 8),    # chunk size beyond the MFMA layouts
+    (ck.F32, 32, 3, 2, 2, 4),
+])
+def test_generic_path(dtype, d, c, Hq, Hkv, w):
+    case = random_case(dtype, [1201], [300], Hq, Hkv, d, w, c, seed=d + c).run()
+    _all_units(case)
+
+
+@pytest.mark.parametrize("Hq,Hkv,w", [(3, 1, 5), (24, 8, 7), (64, 8, 64), (8, 8, 32), (32, 4, 48)])
+def test_mfma_row_blocks(Hq, Hkv, w):
+    # G*w not a multiple of 32 (padding rows), and G*w > 128 (several row
+    # blocks per head: 64/8 heads x w=64 is the 70B shape).
+    case = random_case(ck.BF16, [1500], [160], Hq, Hkv, 128, w, 10, seed=Hq * w).run()
+    _all_units(case)
+
+
+@pytest.mark.parametrize("name,T,l_max,w,c", [
+    ("k_zero_window_only", 700, 9, 32, 10),
+    ("k_covers_all", 700, 700, 32, 10),
+    ("k_above_C", 700, 5000, 32, 10),
+    ("window_is_everything", 96, 10, 96, 10),
+    ("chunk_longer_than_T", 90, 200, 16, 128),
+    ("single_token_window", 333, 50, 1, 10),
+    ("window_plus_one", 33, 10, 32, 10),
+    ("one_chunk_left", 75, 70, 5, 10),
+])
+def test_edge_cases(name, T, l_max, w, c):
+    case = random_case(ck.BF16, [T], [l_max], 8, 2, 128, w, c, seed=T + w).run()
+    _all_units(case)
+    n = case.lengths[0]
+    kk = l_max // c
+    C = -(-T // c)
+    if kk >= C or w == T:
+        assert np.all(n == T)
+    if kk == 0:
+        assert np.all(n == w)
+
+
+def test_ragged_batch_and_many_sequences():
+    # independent sequences packed along the token axis, each with its own
+    # T_b and L_max,b; 11 sequences force several launches per phase.
+    lens = [1000, 2500, 33, 64, 640, 641, 129, 3000, 50, 777, 1024]
+    lmax = [100, 250, 5, 64, 0, 700, 20, 300, 49, 77, 1024]
+    case = random_case(ck.BF16, lens, lmax, 8, 2, 128, 32, 10, seed=5).run()
+    _all_units(case)
+
+
+@pytest.mark.parametrize("n_reuse", [1, 2, 3, 9])
+def test_layer_index_reuse(n_reuse):
+    # Algorithm 2: anchor layers score, the others gather their own K/V with
+    # the anchor's indices.  The workspace holds one scoring layer only, so
+    # anchors are scored in several launches.
+    case = random_case(ck.BF16, [900, 1300], [90, 200], 8, 2, 128, 16, 10, n_layers=5,
+                       n_reuse=n_reuse, seed=n_reuse, n_score_layers=1).run()
+    _all_units(case)
+    assert case.scores.shape[0] == -(-5 // n_reuse)
+
+
+def test_strided_kv_layout():
+    # K/V with a padded head stride (d + 64 elements) and token stride.
+    Hkv, d, T = 2, 128, 1100
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    big_k = torch.randn((1, T, Hkv, d + 64), generator=g, device="cuda").to(torch.bfloat16)
+    big_v = torch.randn((1, T, Hkv, d + 64), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((1, 1, 32, 8, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = big_k[..., :d]
+    v = big_v[..., :d]
+    case = Case(ck.BF16, [T], [110], 8, Hkv, d, 32, 10, 1, q, big_k, big_v,
+                kv_strides=(Hkv * (d + 64), d + 64))
+    case.run()
+    # the oracle sees the logical [T, Hkv, d] view
+    case.k, case.v = k.contiguous(), v.contiguous()
+    _all_units(case)
+
+
+def test_per_layer_entry_points_match_driver():
+    # chunkkv_score / chunkkv_select / chunkkv_gather called one by one give
+    # bit-identical results to chunkkv_compress_layers on the same layer.
+    case = random_case(ck.BF16, [1500, 700], [150, 70], 32, 8, 128, 32, 10, seed=3).run()
+    pl = case.plan
+    ws_n = ck.workspace_bytes(case.prob, 1)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    scores = torch.empty(pl["scores_elems"], dtype=torch.float32, device="cuda")
+    idx = torch.full((pl["index_elems"],), POISON_INDEX, dtype=torch.int32, device="cuda")
+    lens = torch.empty(pl["length_elems"], dtype=torch.int32, device="cuda")
+    ko = torch.empty((pl["index_elems"], 128), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    ck.score(case.prob, case.q_win[0], case.k[0], scores, ws, ws_n)
+    ck.select(case.prob, scores, idx, lens)
+    ck.gather(case.prob, case.k[0], case.v[0], idx, lens, ko, vo)
+    torch.cuda.synchronize()
+    assert np.array_equal(scores.cpu().numpy(), case.scores[0])
+    assert np.array_equal(idx.cpu().numpy(), case.indices[0])
+    assert np.array_equal(lens.cpu().numpy(), case.lengths[0])
+    for b in range(2):
+        for h in range(8):
+            o = pl["index_off"][b] + h * pl["l_cap"][b]
+            n = int(case.lengths[0][b * 8 + h])
+            assert torch.equal(ko[o:o + n], case.bufs.k_out[0, o:o + n])
+            assert torch.equal(vo[o:o + n], case.bufs.v_out[0, o:o + n])
+
+
+def test_deterministic():
+    a = random_case(ck.BF16, [2000], [200], 32, 8, 128, 32, 10, seed=9).run()
+    s1, i1 = a.scores.copy(), a.indices.copy()
+    a.run()
+    assert np.array_equal(s1, a.scores) and np.array_equal(i1, a.indices)
+
+
+def test_phase_events():
+    case = random_case(ck.BF16, [4096], [400], 32, 8, 128, 32, 10, n_layers=4, n_reuse=2, seed=2)
+    ev = ck.PhaseEvents()
+    case.run(phase_events=ev)
+    times = [ev.elapsed_ms(i, i + 1) for i in range(ck.N_PHASE_EVENTS - 1)]
+    assert all(t >= 0 for t in times) and ev.elapsed_ms(0, ck.N_PHASE_EVENTS - 1) > 0
+
+
+# -------------------------------------------------------- workload sizes --
+
+def _props_all_units(case):
+    """Properties that hold for every unit at any size."""
+    G = case.Hq // case.Hkv
+    for a in range(case.scores.shape[0]):
+        for b, T in enumerate(case.seq_lens):
+            C, kk = case.C(b), case.kk(b)
+            for h in range(case.Hkv):
+                s = case.gpu_scores(a * case.n_reuse, b, h).astype(np.float64)
+                assert abs(s.sum() - G * case.w) <= RTOL[case.dtype] * G * case.w
+                idx, _ = case.gpu_indices(a * case.n_reuse, b, h)
+                assert np.array_equal(idx, oracle.indices(T, case.w, case.c, oracle.topk(s, kk)))
+
+
+def _gather_all_layers_on_gpu(case):
+    """Bit-exact gather check of every layer, sequence and head on the GPU."""
+    for l in range(case.L):
+        a = l // case.n_reuse
+        for b in range(len(case.seq_lens)):
+            s0 = int(case.starts[b])
+            for h in range(case.Hkv):
+                idx, _ = case.gpu_indices(l, b, h)
+                it = torch.from_numpy(idx.astype(np.int64)).cuda() + s0
+                o = case.plan["index_off"][b] + h * case.plan["l_cap"][b]
+                for t, out in ((case.k, case.bufs.k_out), (case.v, case.bufs.v_out)):
+                    ref = t[l, :, h, :].index_select(0, it)
+                    got = out[l, o:o + idx.size]
+                    assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), (l, b, h)
+
+
+def test_llama3_8b_layer_T8192():
+    wl = kvsynth.WORKLOADS["llama3-8b-1layer-T8192"]
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    case = Case(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window,
+                wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
+    _all_units(case)
+
+
+def test_llama3_8b_32layer_T32768_sampled():
+    # The workload the benchmark times, in the same launch configuration.
+    wl = kvsynth.WORKLOADS["llama3-8b-32layer-T32768"]
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    case = Case(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window,
+                wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
+    _props_all_units(case)
+    _gather_all_layers_on_gpu(case)
+    jobs = {(a, h): POOL.submit(oracle.chunk_scores, case.host_q(a, 0), case.host_kv(case.k, a, 0),
+                                h, case.Hq, case.w, case.c) for a in (0, 30) for h in (0, 7)}
+    for (a, h), fut in jobs.items():
+        s_ref = fut.result()
+        for l in (a, a + 1):
+            check_unit(case, l, 0, h, s_ref=s_ref)
+
+
+def test_chunk_size_sweep_T16384():
+    wl = kvsynth.WORKLOADS["llama3-8b-csweep-T16384"]
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    refs = {}
+    for c in kvsynth.CSWEEP_CHUNKS:
+        for h in (0, 5):
+            refs[(c, h)] = POOL.submit(oracle.chunk_scores, kvsynth.host_array(cache["q_win"][0, 0]),
+                                       kvsynth.host_array(cache["k"][0]), h, wl.n_q_heads, wl.window, c)
+    for c in kvsynth.CSWEEP_CHUNKS:
+        for l_max in kvsynth.CSWEEP_LMAX:
+            case = Case(ck.BF16, wl.seq_lens, (l_max,), wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                        wl.window, c, 1, cache["q_win"], cache["k"], cache["v"]).run()
+            _props_all_units(case)
+            for h in (0, 5):
+                check_unit(case, 0, 0, h, s_ref=refs[(c, h)].result())
+
+
+def test_llama70b_batch_sampled():
+    # 70B-shaped batch (64 query heads, 8 KV heads, w=64, four sequences of
+    # 131072/65536/32768/16384 tokens in one launch, 20% budget, reuse 2);
+    # 4 of the 80 layers.
+    wl = kvsynth.WORKLOADS["llama-70b-80layer-4seq"].with_(n_layers=4)
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    case = Case(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window,
+                wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
+    _props_all_units(case)
+    _gather_all_layers_on_gpu(case)
+    jobs = {(a, b, h): POOL.submit(oracle.chunk_scores, case.host_q(a, b), case.host_kv(case.k, a, b),
+                                   h, case.Hq, case.w, case.c) for (a, b, h) in ((0, 3, 0), (2, 3, 7), (0, 2, 3))}
+    for (a, b, h), fut in jobs.items():
+        s_ref = fut.result()
+        for l in (a, a + 1):
+            check_unit(case, l, b, h, s_ref=s_ref)
