@@ -39,7 +39,29 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--cpu-anchor-pairs", type=int, default=2,
                     help="oracle sample: this many (scoring, reusing) layer pairs, all KV heads")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB "
+                         "(reference kernel for scaling the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the factor between counter readings and bytes moved."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps, "ms": ms,
+                      "copy_gbps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def cpu_baseline(wl, cache, n_pairs: int):
@@ -90,6 +112,10 @@ def main():
 
     import torch
 
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+
     import kvsynth
     from kv_cache_compression_win_amd import accounting
     from kv_cache_compression_win_amd import chunkkv as ck
@@ -137,8 +163,7 @@ def main():
     def mean_ms(i, j):
         return sum(e.elapsed_ms(i, j) for e in evs) / len(evs)
 
-    ph = {"score": mean_ms(0, 1), "combine": mean_ms(1, 2), "select": mean_ms(2, 3),
-          "gather": mean_ms(3, 4)}
+    ph = {"score": mean_ms(0, 1), "combine_select": mean_ms(1, 2), "gather": mean_ms(2, 3)}
 
     # algorithmic bytes (kept-token counts from the actual lengths)
     n_anchor = bufs.n_anchor

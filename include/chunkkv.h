@@ -113,7 +113,7 @@ typedef struct {
 } chunkkv_sizes;
 
 /* Number of phase events chunkkv_compress_layers can record. */
-#define CHUNKKV_N_PHASE_EVENTS 5
+#define CHUNKKV_N_PHASE_EVENTS 4
 
 /*
  * Host-only planning: validates the problem and fills the sizes and, when
@@ -188,8 +188,11 @@ int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
  *                   a larger one lets more anchor layers share a launch
  *   phase_events    NULL, or HOST [CHUNKKV_N_PHASE_EVENTS] hipEvent_t handles
  *                   recorded on `stream` before the score kernels, after
- *                   them, after the score-combine kernels, after selection
- *                   and after the gathers (for timing; any entry may be NULL)
+ *                   them, after the combine + selection kernels and after
+ *                   the gathers (for timing; any entry may be NULL).  When
+ *                   the workspace cannot hold every scoring layer at once,
+ *                   the phases interleave and entry 1 is recorded together
+ *                   with entry 2.
  * Errors: INVALID_ARG (incl. n_layers < 1, n_reuse < 1, a NULL table entry
  * that is needed), UNSUPPORTED, WORKSPACE, HIP.
  */

@@ -27,32 +27,34 @@ def hipcc() -> str:
     return path if os.path.exists(path) else (shutil.which("hipcc") or "hipcc")
 
 
-def common_flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+def common_flags(defines=()):
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", *defines,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(defines), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(lib: str = LIB, build_dir: str = BUILD_DIR, defines=()) -> str:
+    """Compile and link.  `defines` (e.g. "-DCKV_GATHER_ROWS=128") override the
+    compile-time tuning constants; `lib`/`build_dir` place a variant build."""
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

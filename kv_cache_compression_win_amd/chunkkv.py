@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libchunkkv.so")
 
 F32, BF16 = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-N_PHASE_EVENTS = 5
+N_PHASE_EVENTS = 4
 
 SYMBOLS = ("chunkkv_plan", "chunkkv_workspace_bytes", "chunkkv_score", "chunkkv_select",
            "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_last_error")
@@ -103,8 +103,8 @@ def hip_runtime() -> ctypes.CDLL:
 class PhaseEvents:
     """CHUNKKV_N_PHASE_EVENTS raw hipEvent_t handles for chunkkv_compress_layers'
     phase_events argument: recorded on the launch stream before the score
-    kernels, after them, after the combine kernels, after selection and after
-    the gathers."""
+    kernels, after them, after the combine + selection kernels and after the
+    gathers."""
 
     def __init__(self):
         H = hip_runtime()

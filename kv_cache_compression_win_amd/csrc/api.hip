@@ -210,22 +210,25 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
 
 hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float* scores,
                        hipStream_t s) {
+  const int spb = combine_spans_per_blk(pl.R_pad);
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
     CombineParams P{};
     P.n_layers = nl;
     P.n_seqs = nb;
     P.span_chunks = pl.span_chunks;
+    P.spans_per_blk = spb;
     int items = 0;
     for (int i = 0; i < nb; ++i) {
       const Seq& sq = pl.seq[b0 + i];
       P.C[i] = sq.C;
       P.n_span[i] = sq.n_span;
+      P.n_blk[i] = (sq.n_span + spb - 1) / spb;
       P.item0[i] = items;
       P.u_off[i] = sq.u_off;
       P.st_off[i] = sq.st_off;
       P.score_off[i] = sq.score_off;
-      items += pl.Hkv * sq.n_span;
+      items += pl.Hkv * P.n_blk[i];
     }
     P.item0[nb] = items;
     P.items_per_layer = items;
@@ -465,13 +468,12 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
     if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
     if ((e = run_combine(pl, na, U, st, scores + a0 * pl.scores_elems, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
+    if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
+                        lengths + a0 * pl.length_elems, s)) != hipSuccess)
+      return hip_fail(e, "select launch");
   }
   if (!one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
   if ((e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
-
-  if ((e = run_select(pl, n_anchor, scores, indices, lengths, s)) != hipSuccess)
-    return hip_fail(e, "select launch");
-  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
 
   int32_t blocks[kMaxLayers];
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
@@ -481,7 +483,7 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
         hipSuccess)
       return hip_fail(e, "gather launch");
   }
-  if ((e = record(4)) != hipSuccess) return hip_fail(e, "phase event");
+  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
   return ok();
 }
 

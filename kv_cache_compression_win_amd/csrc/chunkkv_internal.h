@@ -14,7 +14,18 @@ constexpr int kMaxSeqs = 8;
 
 constexpr int kThreads = 256;            // every kernel: 4 wave64s per workgroup
 constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score workgroup
-constexpr int kGatherRows = 64;          // output rows per gather workgroup
+#ifndef CKV_GATHER_ROWS
+#define CKV_GATHER_ROWS 64
+#endif
+#ifndef CKV_SPAN_TARGET
+#define CKV_SPAN_TARGET 64
+#endif
+#ifndef CKV_MAX_TILES
+#define CKV_MAX_TILES 5
+#endif
+constexpr int kGatherRows = CKV_GATHER_ROWS;   // output rows per gather workgroup
+constexpr int kSpanTarget = CKV_SPAN_TARGET;   // chunks per MFMA score work item (LDS-resident)
+constexpr int kMaxTiles = CKV_MAX_TILES;       // 32-slot MFMA tiles per group, at most
 
 // A chunk-partial reference is rebased only when a new maximum exceeds the
 // current reference by this many powers of two; below that, exp2 of the
@@ -36,6 +47,7 @@ struct ScoreParams {
   int32_t n_seqs;
   int32_t items_per_layer;
   int32_t span_chunks;
+  int32_t n_workers;            // MFMA path: persistent workgroups (contiguous item ranges)
   int64_t tok0[kMaxSeqs];       // first K/V token row of sequence b
   int32_t qseq[kMaxSeqs];       // sequence index for q_stride_seq
   int32_t T[kMaxSeqs];
@@ -55,15 +67,19 @@ struct ScoreParams {
 };
 
 // --------------------------------------------------------------- combine --
-// Item = (layer, b, h, span): S_j = sum_r U[j][r] * 2^((m_s,r - M_r)*scale) / L_r
-// with M_r, L_r the row's log-sum-exp over all spans of the head.
+// Item = (layer, b, h, block of spans_per_blk spans): every item first forms
+// the log-sum-exp (M_r, L_r) of all rows from the span statistics, then
+//   S_j = sum_r U[j][r] * 2^((m_s,r - M_r)*scale) / L_r
+// for the chunks of its spans.
 struct CombineParams {
   int32_t n_layers;
   int32_t n_seqs;
   int32_t items_per_layer;
   int32_t span_chunks;
+  int32_t spans_per_blk;
   int32_t C[kMaxSeqs];
   int32_t n_span[kMaxSeqs];
+  int32_t n_blk[kMaxSeqs];      // span blocks per head
   int32_t item0[kMaxSeqs + 1];
   int64_t u_off[kMaxSeqs];
   int64_t st_off[kMaxSeqs];
@@ -77,8 +93,12 @@ struct CombineParams {
 };
 
 // ---------------------------------------------------------------- select --
-// Item = (scoring layer, b, h).  Radix top-k over fp32 score bit patterns,
-// recent-window merge, ascending index list.
+// Item = (scoring layer, b, h), one workgroup of kSelectThreads: top-k
+// threshold on the fp32 score bit patterns, recent-window merge, ascending
+// index list.
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectKeysPerThread = 16;   // scores held in registers: C <= 16384
+
 struct SelectParams {
   int32_t n_layers;
   int32_t n_seqs;
@@ -125,11 +145,13 @@ struct GatherParams {
 // MFMA path: bf16, head_dim 128, chunk size with a static layout.
 bool score_mfma_supported(int chunk);
 int score_mfma_span_chunks(int chunk);
-hipError_t launch_score_mfma(const ScoreParams& p, int n_blocks, hipStream_t s);
+// Launches min(n_items, resident workgroups) persistent workgroups.
+hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s);
 // Generic path: any dtype / head_dim / chunk size (VALU fp32).
 int score_generic_span_chunks(int R_pad, int chunk);
 size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d);
 hipError_t launch_score_generic(const ScoreParams& p, int dtype, int n_blocks, hipStream_t s);
+int combine_spans_per_blk(int R_pad);
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s);

@@ -6,64 +6,72 @@
 //   M_r = max_s m_s,  L_r = sum_s 2^((m_s - M_r) * scale) * l_s,
 // and a chunk j of span s scores
 //   S_j = sum_r U[j][r] * 2^((m_s,r - M_r) * scale) / L_r.
-// Work item = (layer, sequence, KV head, span); rows are summed in a fixed
-// order (lane-strided, then a fixed butterfly), so results are deterministic.
-#include "chunkkv_internal.h"
+// Work item = (layer, sequence, KV head, block of spans): enough items to
+// fill the GPU.  Each item forms (M_r, L_r) itself from the statistics (a few
+// percent of the U bytes it reads) and then streams its chunks' U rows with
+// eight 16-byte loads in flight per thread.  The row sums follow the fixed
+// order of combine_chunks: results are deterministic.
+#include "lse_combine.h"
 
 namespace ckv {
 namespace {
 
 constexpr int kMaxRows = 4096;
+constexpr int kWeightFloats = 4096;   // weights of one item's spans (16 KB)
 
+template <int QPT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
-  __shared__ float wts[kMaxRows];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float2 lse[kMaxRows];
+  __shared__ float wts[kWeightFloats];
+  const int tid = threadIdx.x;
 
   const int li = blockIdx.x / P.items_per_layer;
   int item = blockIdx.x - li * P.items_per_layer;
   int b = 0;
   while (b + 1 < P.n_seqs && item >= P.item0[b + 1]) ++b;
   item -= P.item0[b];
-  const int nspan = P.n_span[b];
-  const int span = item % nspan;
-  const int h = item / nspan;
-  const int C = P.C[b];
+  const int nblk = P.n_blk[b];
+  const int blk = item % nblk;
+  const int h = item / nblk;
+  const int C = P.C[b], nspan = P.n_span[b];
 
   const float2* st = P.stats + li * P.st_layer_stride + P.st_off[b] +
                      static_cast<int64_t>(h) * nspan * P.R_pad;
-  for (int r = tid; r < P.R; r += kThreads) {
-    float M = -INFINITY;
-    for (int s = 0; s < nspan; ++s) M = fmaxf(M, st[static_cast<int64_t>(s) * P.R_pad + r].x);
-    float L = 0.0f;
-    for (int s = 0; s < nspan; ++s) {
-      const float2 ml = st[static_cast<int64_t>(s) * P.R_pad + r];
-      L += __builtin_amdgcn_exp2f((ml.x - M) * P.scale) * ml.y;
-    }
-    const float m_this = st[static_cast<int64_t>(span) * P.R_pad + r].x;
-    wts[r] = __builtin_amdgcn_exp2f((m_this - M) * P.scale) / L;
+  rows_lse<kThreads>(st, nspan, P.R, P.R_pad, P.scale, lse);
+  __syncthreads();
+  const int s_lo = blk * P.spans_per_blk;
+  const int ns = min(P.spans_per_blk, nspan - s_lo);
+  for (int e = tid; e < ns * P.R_pad; e += kThreads) {
+    const int s = e / P.R_pad, r = e - s * P.R_pad;
+    wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse[r], P.scale)
+                     : 0.0f;
   }
   __syncthreads();
 
-  const int j0 = span * P.span_chunks;
-  const int nch = min(P.span_chunks, C - j0);
-  const float* U = P.U + li * P.u_layer_stride + P.u_off[b] +
-                   (static_cast<int64_t>(h) * C + j0) * P.R_pad;
-  float* S = P.scores + li * P.score_layer_stride + P.score_off[b] + static_cast<int64_t>(h) * C + j0;
-  for (int j = wave; j < nch; j += 4) {
-    const float* u = U + static_cast<int64_t>(j) * P.R_pad;
-    float acc = 0.0f;
-    for (int r = lane; r < P.R; r += 64) acc = fmaf(u[r], wts[r], acc);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) S[j] = acc;
-  }
+  const float* U = P.U + li * P.u_layer_stride + P.u_off[b] + static_cast<int64_t>(h) * C * P.R_pad;
+  float* S = P.scores + li * P.score_layer_stride + P.score_off[b] + static_cast<int64_t>(h) * C;
+  const int j_lo = s_lo * P.span_chunks;
+  const int j_hi = min(C, (s_lo + ns) * P.span_chunks);
+  combine_chunks<kThreads, QPT>(U, wts, j_lo, j_hi, s_lo, P.span_chunks, P.R_pad, S);
 }
 
 }  // namespace
 
+int combine_spans_per_blk(int R_pad) {
+  const int spb = kWeightFloats / R_pad;
+  return spb < 1 ? 1 : (spb > 4 ? 4 : spb);
+}
+
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
-  if (p.R > kMaxRows) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p);
+  if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
+  switch (combine_qpt(p.R_pad)) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -13,7 +13,10 @@
 namespace ckv {
 namespace {
 
-constexpr int kUnroll = 4;
+#ifndef CKV_GATHER_UNROLL
+#define CKV_GATHER_UNROLL 4
+#endif
+constexpr int kUnroll = CKV_GATHER_UNROLL;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) {
