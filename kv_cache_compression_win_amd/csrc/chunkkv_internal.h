@@ -21,11 +21,18 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #define CKV_SPAN_TARGET 64
 #endif
 #ifndef CKV_MAX_TILES
-#define CKV_MAX_TILES 5
+#define CKV_MAX_TILES 4
+#endif
+#ifndef CKV_STAGE_TILES
+#define CKV_STAGE_TILES 8
+#endif
+#ifndef CKV_MIN_WAVES
+#define CKV_MIN_WAVES 2
 #endif
 constexpr int kGatherRows = CKV_GATHER_ROWS;   // output rows per gather workgroup
 constexpr int kSpanTarget = CKV_SPAN_TARGET;   // chunks per MFMA score work item (LDS-resident)
 constexpr int kMaxTiles = CKV_MAX_TILES;       // 32-slot MFMA tiles per group, at most
+constexpr int kStageTiles = CKV_STAGE_TILES;   // key tiles in flight per workgroup (register ring)
 
 // A chunk-partial reference is rebased only when a new maximum exceeds the
 // current reference by this many powers of two; below that, exp2 of the
@@ -47,7 +54,11 @@ struct ScoreParams {
   int32_t n_seqs;
   int32_t items_per_layer;
   int32_t span_chunks;
-  int32_t n_workers;            // MFMA path: persistent workgroups (contiguous item ranges)
+  // MFMA path work split: each unit (layer, b, h, row block) of sequence b
+  // is cut into wpu[b] balanced span ranges, one per workgroup
+  int32_t wpu[kMaxSeqs];
+  int32_t worker0[kMaxSeqs + 1];
+  int32_t workers_per_layer;
   int64_t tok0[kMaxSeqs];       // first K/V token row of sequence b
   int32_t qseq[kMaxSeqs];       // sequence index for q_stride_seq
   int32_t T[kMaxSeqs];

@@ -13,6 +13,8 @@
 // kernel writes, per query row, the chunk partials
 //   U[j][r] = sum_{t in chunk j} 2^((x_rt - m_r) * log2(e)/sqrt(d))
 // and (m_r, l_r = sum over the span) for the log-sum-exp combine.
+#include <type_traits>
+
 #include "chunkkv_internal.h"
 
 namespace ckv {
@@ -20,24 +22,31 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Explicitly global-address-space element types, so that loads through
+// addresses kept in LDS compile to global (not flat) instructions.
+typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 
 constexpr int kD = 128;              // head_dim of this path
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
-// Number of 32-slot MFMA tiles per group for chunk size c: the least padding
-// (slots per lane half = 16 * nt, holding floor(16 * nt / c) whole chunks),
-// ties to the smaller tile count, at most kMaxTiles tiles.
+// Number of 32-slot MFMA tiles per group for chunk size c (slots per lane
+// half = 16 * nt, holding floor(16 * nt / c) whole chunks): the smallest
+// count whose padding is at most 1/16 of the slots, else the one with the
+// least padding (ties to fewer tiles), at most kMaxTiles.
 constexpr int pick_tiles(int c) {
-  int best = 0, best_waste_num = 1, best_waste_den = 0;  // waste = num/den
+  int best = 0, best_num = 1, best_den = 0;  // padding = num/den
   for (int nt = 1; nt <= kMaxTiles; ++nt) {
     const int cph = 16 * nt / c;
     if (cph == 0) continue;
     const int num = 16 * nt - cph * c, den = 16 * nt;
-    if (best == 0 || num * best_waste_den < best_waste_num * den) {
+    if (num * 16 <= den) return nt;
+    if (best == 0 || num * best_den < best_num * den) {
       best = nt;
-      best_waste_num = num;
-      best_waste_den = den;
+      best_num = num;
+      best_den = den;
     }
   }
   return best;
@@ -54,6 +63,8 @@ struct Geo {
   static constexpr int GPS = (kSpanTarget / GROUP_CHUNKS) > 0 ? (kSpanTarget / GROUP_CHUNKS) : 1;
   static constexpr int SPAN_CHUNKS = GROUP_CHUNKS * GPS;
   static constexpr int LOADS = NT * 32 * kPieces / kThreads;  // uint4 per thread per group
+  // register stages (groups of keys in flight), at least 2
+  static constexpr int STAGES = (kStageTiles / NT) >= 2 ? (kStageTiles / NT > 4 ? 4 : kStageTiles / NT) : 2;
 };
 
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
@@ -111,45 +122,115 @@ struct Item {
   int li, b, h, rb, span, nspan, C, tok_begin, tok_end, ngroups;
 };
 
+// The launch's per-layer and per-sequence tables, copied to LDS once so that
+// decoding an item with a runtime index never issues a vector memory load
+// (those would share the counter the key stream is waited on with).
+struct Tables {
+  uint64_t q[kMaxLayers];        // device addresses (global address space)
+  uint64_t k[kMaxLayers];
+  int64_t tok0[kMaxSeqs];
+  int64_t u_off[kMaxSeqs];
+  int64_t st_off[kMaxSeqs];
+  int32_t item0[kMaxSeqs + 1];
+  int32_t n_span[kMaxSeqs];
+  int32_t T[kMaxSeqs];
+  int32_t C[kMaxSeqs];
+  int32_t qseq[kMaxSeqs];
+  int32_t wpu[kMaxSeqs];
+  int32_t worker0[kMaxSeqs + 1];
+};
+
+__device__ __forceinline__ void load_tables(const ScoreParams& P, Tables& t) {
+  const int i = threadIdx.x;
+  if (i < kMaxLayers) {
+    t.q[i] = reinterpret_cast<uint64_t>(P.q[i]);
+    t.k[i] = reinterpret_cast<uint64_t>(P.k[i]);
+  }
+  if (i < kMaxSeqs) {
+    t.tok0[i] = P.tok0[i];
+    t.u_off[i] = P.u_off[i];
+    t.st_off[i] = P.st_off[i];
+    t.n_span[i] = P.n_span[i];
+    t.T[i] = P.T[i];
+    t.C[i] = P.C[i];
+    t.qseq[i] = P.qseq[i];
+    t.wpu[i] = P.wpu[i];
+  }
+  if (i <= kMaxSeqs) {
+    t.item0[i] = P.item0[i];
+    t.worker0[i] = P.worker0[i];
+  }
+}
+
 template <int CC>
-__device__ __forceinline__ Item decode_item(const ScoreParams& P, int flat) {
+__device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& t, int flat) {
   using G = Geo<CC>;
   Item it;
   it.li = flat / P.items_per_layer;
   int item = flat - it.li * P.items_per_layer;
   int b = 0;
-  while (b + 1 < P.n_seqs && item >= P.item0[b + 1]) ++b;
-  item -= P.item0[b];
+  while (b + 1 < P.n_seqs && item >= t.item0[b + 1]) ++b;
+  item -= t.item0[b];
   it.b = b;
-  it.nspan = P.n_span[b];
+  it.nspan = t.n_span[b];
   it.span = item % it.nspan;
   const int hr = item / it.nspan;
   it.rb = hr % P.n_rb;
   it.h = hr / P.n_rb;
-  it.C = P.C[b];
+  it.C = t.C[b];
   it.tok_begin = it.span * G::SPAN_CHUNKS * CC;
-  it.tok_end = min(P.T[b], it.tok_begin + G::SPAN_CHUNKS * CC);
+  it.tok_end = min(t.T[b], it.tok_begin + G::SPAN_CHUNKS * CC);
   it.ngroups = (it.tok_end - it.tok_begin + G::GROUP_TOK - 1) / G::GROUP_TOK;
   return it;
 }
 
-// Persistent workgroups: workgroup w takes the contiguous range of work items
-// [w*N/W, (w+1)*N/W) (consecutive spans of the same head, so the window-query
-// fragments change rarely) and keeps one group of keys in flight across item
-// boundaries: while group g is multiplied and reduced, group g+1 -- of the
-// same item or of the next one -- is already being loaded.
+// Position in a workgroup's stream of key groups.
+struct Cursor {
+  int flat, g;
+  Item it;
+};
+
 template <int CC>
-__global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScoreParams P) {
+__device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& t, Cursor& c, int hi) {
+  if (++c.g == c.it.ngroups) {
+    c.g = 0;
+    if (++c.flat >= hi) return false;
+    c.it = decode_item<CC>(P, t, c.flat);
+  }
+  return true;
+}
+
+// Each workgroup takes a balanced range of consecutive spans of ONE unit
+// (layer, sequence, KV head, row block), so its window-query fragments are
+// loaded once.  Its key groups form one stream, loaded through a ring of
+// STAGES register stages: while group k is multiplied and reduced,
+// groups k+1 .. k+STAGES-1 -- of this item or the next ones -- are in flight.
+// The ring is indexed statically (the loop is unrolled by STAGES), so each
+// LDS store waits only for the loads of its own stage.
+template <int CC>
+__global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
-  __shared__ uint4 k_lds[G::NT * 32 * kPieces];
+  __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
   __shared__ float u_lds[G::SPAN_CHUNKS * kMfmaRows];
+  __shared__ Tables tab;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, ho = lane >> 5;
-  const int total = P.n_layers * P.items_per_layer;
-  const int lo = static_cast<int>(static_cast<int64_t>(blockIdx.x) * total / P.n_workers);
-  const int hi = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * total / P.n_workers);
+  load_tables(P, tab);
+  __syncthreads();
+  int lo, hi;
+  {
+    const int li = blockIdx.x / P.workers_per_layer;
+    const int wr = blockIdx.x - li * P.workers_per_layer;
+    int b = 0;
+    while (b + 1 < P.n_seqs && wr >= tab.worker0[b + 1]) ++b;
+    const int wpu = tab.wpu[b], ns = tab.n_span[b];
+    const int unit = (wr - tab.worker0[b]) / wpu, piece = (wr - tab.worker0[b]) % wpu;
+    const int base = li * P.items_per_layer + tab.item0[b] + unit * ns;
+    lo = base + piece * ns / wpu;
+    hi = base + (piece + 1) * ns / wpu;
+  }
   if (lo >= hi) return;
 
   // window-query fragments (B operand) of this wave's 32 rows; rows >= R are zero
@@ -160,10 +241,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScorePara
       const int g = r / P.w;
       const int rr = r - g * P.w;
       const int hq = it.h * P.G + g;
-      const __bf16* qp = static_cast<const __bf16*>(P.q[it.li]) + P.qseq[it.b] * P.q_ss + rr * P.q_sr +
-                         hq * P.q_sh + ho * (kD / 2);
+      const uint64_t qa = tab.q[it.li] + 2 * static_cast<uint64_t>(tab.qseq[it.b] * P.q_ss + rr * P.q_sr +
+                                                                   hq * P.q_sh + ho * (kD / 2));
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(qp + 8 * s);
+      for (int s = 0; s < kKSteps; ++s) bq[s] = *((gbf16x8*)(qa + 16 * s));
     } else {
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s) bq[s] = bf16x8{};
@@ -171,32 +252,32 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScorePara
   };
 
   // key streaming: slot (tile tau, row i) <-> token of lane half (i/4)%2.
-  // Rows past the end of the span are loaded clamped (their logits are masked).
-  uint4 regs[G::LOADS];
+  // Every slot is loaded unconditionally: rows past the end of the span are
+  // clamped to its last row and padding slots (lam >= HALF_TOK) to the half's
+  // last slot, so their requests coincide with real ones; their logits are
+  // never used (padding) or masked (past the end).
+  u32x4 regs[G::STAGES][G::LOADS];
   const int64_t st_bytes = P.kv_st * 2;
-  auto load_group = [&](const Item& it, int gi) {
-    const char* kbase = static_cast<const char*>(P.k[it.li]) +
-                        (P.tok0[it.b] * P.kv_st + static_cast<int64_t>(it.h) * P.kv_sh) * 2;
+  auto load_group = [&](u32x4 (&dst)[G::LOADS], const Item& it, int gi) {
+    const uint64_t kbase = tab.k[it.li] + 2 * static_cast<uint64_t>(tab.tok0[it.b] * P.kv_st +
+                                                                    static_cast<int64_t>(it.h) * P.kv_sh);
     const int gtok0 = it.tok_begin + gi * G::GROUP_TOK;
 #pragma unroll
     for (int x = 0; x < G::LOADS; ++x) {
       const int gp = x * kThreads + tid;
       const int sr = gp / kPieces, p = gp % kPieces;
       const int tau = sr >> 5, i = sr & 31;
-      const int lam = 16 * tau + 4 * (i >> 3) + (i & 3);
+      const int lam = min(16 * tau + 4 * (i >> 3) + (i & 3), G::HALF_TOK - 1);
       const int tok = min(gtok0 + ((i >> 2) & 1) * G::HALF_TOK + lam, it.tok_end - 1);
-      if (lam < G::HALF_TOK)
-        regs[x] = *reinterpret_cast<const uint4*>(kbase + tok * st_bytes + p * 16);
-      else
-        regs[x] = make_uint4(0u, 0u, 0u, 0u);
+      dst[x] = *((gu32x4*)(kbase + tok * st_bytes + p * 16));
     }
   };
-  auto store_group = [&]() {
+  auto store_group = [&](const u32x4 (&src)[G::LOADS]) {
 #pragma unroll
     for (int x = 0; x < G::LOADS; ++x) {
       const int gp = x * kThreads + tid;
       const int sr = gp / kPieces, p = gp % kPieces;
-      k_lds[sr * kPieces + (p ^ (sr & 15))] = regs[x];
+      k_lds[sr * kPieces + (p ^ (sr & 15))] = src[x];
     }
   };
   // per-row span statistics and chunk partials of a finished item
@@ -204,11 +285,11 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScorePara
     const int r = it.rb * kMfmaRows + wave * 32 + n;
     const float l_row = l_acc + shfl_xor32(l_acc);
     if (ho == 0 && r < P.R)
-      P.stats[it.li * P.st_layer_stride + P.st_off[it.b] +
+      P.stats[it.li * P.st_layer_stride + tab.st_off[it.b] +
               (static_cast<int64_t>(it.h) * it.nspan + it.span) * P.R_pad + r] = make_float2(m_ref, l_row);
     __syncthreads();
     const int nch = min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS);
-    float* ug = P.U + it.li * P.u_layer_stride + P.u_off[it.b] +
+    float* ug = P.U + it.li * P.u_layer_stride + tab.u_off[it.b] +
                 (static_cast<int64_t>(it.h) * it.C + it.span * G::SPAN_CHUNKS) * P.R_pad + it.rb * kMfmaRows;
     for (int e = tid; e < nch * (kMfmaRows / 4); e += kThreads) {
       const int j = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
@@ -218,26 +299,33 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScorePara
   };
 
   float* u_row = u_lds + ho * G::CPH * kMfmaRows + wave * 32 + n;
-  int flat = lo, g = 0;
-  Item cur = decode_item<CC>(P, flat);
-  load_q(cur);
-  load_group(cur, 0);
+  Cursor cc{lo, 0, decode_item<CC>(P, tab, lo)};   // group being computed
+  Cursor lc = cc;                             // next group to load
+  // Every step issues exactly one group of loads: past the end of the range
+  // the last group is loaded again (its data is never used), so the number of
+  // loads younger than any stage is fixed and each stage store waits only
+  // for its own loads.
+  auto load_next = [&](u32x4 (&dst)[G::LOADS]) {
+    load_group(dst, lc.it, lc.g);
+    Cursor t = lc;
+    if (cursor_next<CC>(P, tab, t, hi)) lc = t;
+  };
+  load_q(cc.it);
+  // issue the stages strictly in ring order (stage 0 oldest)
+#pragma unroll
+  for (int s = 0; s < G::STAGES; ++s) {
+    load_next(regs[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float m_ref = -INFINITY, l_acc = 0.0f;
-  for (;;) {
+
+  // one group of the stream, held in ring stage S; false when the range ends
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int S = decltype(stage_tag)::value;
     __syncthreads();  // previous group's LDS reads (and any flush) are done
-    store_group();
+    store_group(regs[S]);
     __syncthreads();
-
-    int nflat = flat, ng = g + 1;
-    if (ng == cur.ngroups) {
-      ++nflat;
-      ng = 0;
-    }
-    const bool has_next = nflat < hi;
-    Item nxt = cur;
-    if (has_next && nflat != flat) nxt = decode_item<CC>(P, nflat);
-    if (has_next) load_group(nxt, ng);
-
+    load_next(regs[S]);
     f32x16 acc[G::NT];
 #pragma unroll
     for (int tau = 0; tau < G::NT; ++tau) {
@@ -249,22 +337,23 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(const ScorePara
         acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[tau], 0, 0, 0);
       }
     }
-    const int gtok0 = cur.tok_begin + g * G::GROUP_TOK;
-    const int nvalid = cur.tok_end - (gtok0 + ho * G::HALF_TOK);
-    group_softmax<CC>(acc, gtok0 + G::GROUP_TOK <= cur.tok_end, nvalid, P.scale, P.rebase_raw, m_ref,
-                      l_acc, u_row, g);
-    if (g + 1 == cur.ngroups) {
-      flush(cur, m_ref, l_acc);
+    const Item& it = cc.it;
+    const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
+    const int nvalid = it.tok_end - (gtok0 + ho * G::HALF_TOK);
+    group_softmax<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, P.rebase_raw, m_ref, l_acc,
+                      u_row, cc.g);
+    if (cc.g + 1 == it.ngroups) {
+      flush(it, m_ref, l_acc);
       m_ref = -INFINITY;
       l_acc = 0.0f;
     }
-    if (!has_next) break;
-    if (nflat != flat) {
-      if (nxt.li != cur.li || nxt.b != cur.b || nxt.h != cur.h || nxt.rb != cur.rb) load_q(nxt);
-      cur = nxt;
-      flat = nflat;
-    }
-    g = ng;
+    return cursor_next<CC>(P, tab, cc, hi);
+  };
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if constexpr (G::STAGES > 1) if (!step(std::integral_constant<int, 1 % G::STAGES>{})) break;
+    if constexpr (G::STAGES > 2) if (!step(std::integral_constant<int, 2 % G::STAGES>{})) break;
+    if constexpr (G::STAGES > 3) if (!step(std::integral_constant<int, 3 % G::STAGES>{})) break;
   }
 }
 
@@ -304,9 +393,11 @@ int score_mfma_span_chunks(int chunk) {
   }
 }
 
+// Work split: about one workgroup per resident slot, each a balanced range of
+// consecutive spans of one unit.
 template <int CC>
-hipError_t launch_persistent(ScoreParams p, int n_items, hipStream_t s) {
-  static thread_local int cached_dev = -1, cached_workers = 0;
+hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
+  static thread_local int cached_dev = -1, cached_slots = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -317,17 +408,25 @@ hipError_t launch_persistent(ScoreParams p, int n_items, hipStream_t s) {
         hipSuccess)
       return e;
     cached_dev = dev;
-    cached_workers = cus * (per_cu > 0 ? per_cu : 1);
+    cached_slots = cus * (per_cu > 0 ? per_cu : 1);
   }
-  p.n_workers = n_items < cached_workers ? n_items : cached_workers;
-  hipLaunchKernelGGL(score_mfma_kernel<CC>, dim3(p.n_workers), dim3(kThreads), 0, s, p);
+  const int per_worker = (n_items + cached_slots - 1) / cached_slots;  // spans per workgroup, target
+  int w = 0;
+  for (int b = 0; b < p.n_seqs; ++b) {
+    p.wpu[b] = (p.n_span[b] + per_worker - 1) / per_worker;
+    p.worker0[b] = w;
+    w += p.H_kv * p.n_rb * p.wpu[b];
+  }
+  p.worker0[p.n_seqs] = w;
+  p.workers_per_layer = w;
+  hipLaunchKernelGGL(score_mfma_kernel<CC>, dim3(w * p.n_layers), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <int CC>
 hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s) {
   if constexpr (pick_tiles(CC) >= 1)
-    return launch_persistent<CC>(p, n_items, s);
+    return launch_split<CC>(p, n_items, s);
   else
     return hipErrorInvalidValue;
 }
