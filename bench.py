@@ -29,6 +29,33 @@ METRIC = "KV tokens compressed/sec per layer·head-set + achieved HBM GB/s (% of
 HBM_PEAK_GBPS = 8000.0
 
 
+SCORE_SOURCES = ("kv_cache_compression_win_amd/csrc/score_mfma.hip",
+                 "kv_cache_compression_win_amd/csrc/chunkkv_internal.h")
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per score-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or
+    None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{") and "traffic_bytes_per_launch" in line:
+                rec = json.loads(line)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for rel in SCORE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +221,7 @@ def main():
                    "l_max": list(wl.l_max), "n_reuse": n_reuse, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel", "achieved": score_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
-                     "traffic": None,
+                     "traffic": counted_traffic(wl.name),
                      "algorithmic_bytes_per_launch": score_kernel_bytes,
                      "avg_launch_ms": ph["score"]},
         "step_hbm": {"achieved": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,

@@ -21,8 +21,10 @@ constexpr int kWeightFloats = 4096;   // weights of one item's spans (16 KB)
 
 template <int QPT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
-  __shared__ float2 lse[kMaxRows];
-  __shared__ float wts[kWeightFloats];
+  // dynamic LDS: lse [R_pad] float2, then weights [spans_per_blk][R_pad]
+  extern __shared__ float smem[];
+  float2* lse = reinterpret_cast<float2*>(smem);
+  float* wts = smem + 2 * P.R_pad;
   const int tid = threadIdx.x;
 
   const int li = blockIdx.x / P.items_per_layer;
@@ -64,12 +66,14 @@ int combine_spans_per_blk(int R_pad) {
 
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
   if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
+  const size_t lds = (static_cast<size_t>(2) * p.R_pad + static_cast<size_t>(p.spans_per_blk) * p.R_pad) *
+                     sizeof(float);
   switch (combine_qpt(p.R_pad)) {
-    case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
-    case 16: hipLaunchKernelGGL(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
+    case 16: hipLaunchKernelGGL(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
