@@ -2,19 +2,29 @@
 // section 4.1, Algorithm 1 steps 4-6; the TopK -> index form is Kara eqs.
 // (2)-(3)).
 //
-// Work item = (scoring layer, sequence, KV head), one workgroup of 1024
-// threads (16 waves).
-//  1. Threshold: the scores are >= 0, so the unsigned order of their fp32 bit
-//     patterns is the value order.  tau = the largest 32-bit pattern v with
-//     #{S_j >= v} >= k is built greedily from the top bit, two bits per
-//     workgroup-wide count; it is exactly the k-th largest score.
-//     Scores stay in registers (16 per thread) when C <= 16384.
-//  2. One ordered pass over the chunks: a chunk is selected if its score is
-//     above tau, or equal to tau and among the first k - #{S > tau} equal ones
-//     in id order (lower chunk id first).  Each chunk contributes all its
-//     tokens (selected) or its overlap with the recent window [T-w, T); an
-//     exclusive scan over the chunks places every kept token, so the index
-//     list is ascending and duplicate-free.
+// Threshold: the scores are >= 0, so the unsigned order of their fp32 bit
+// patterns is the value order.  tau = the largest 32-bit pattern v with
+// #{S_j >= v} >= k is built greedily from the top bit (bit 30 alone, then two
+// bits per workgroup-wide count of three candidates); it is exactly the k-th
+// largest score.  A chunk is selected if its score is above tau, or equal to
+// tau and among the first k - #{S > tau} equal ones in id order (lower chunk
+// id first).
+//
+// Index list: with j_w = floor((T - w) / c), the first chunk that reaches the
+// recent window [T - w, T), the kept tokens in ascending order are the c
+// tokens of every selected chunk j < j_w, followed by the contiguous tail
+// [j_w * c, T) if chunk j_w is selected, else [T - w, T) (a selected chunk
+// after j_w lies inside the window).  So n = m * c + |tail| with m the number
+// of selected chunks before j_w.
+//
+// Two kernels, one workgroup per (scoring layer, sequence, KV head):
+//   select_fast_kernel  256 threads, C <= 8192: scores in registers
+//     (chunk j in slot j / 256 of thread j % 256), counts by wave ballots,
+//     one barrier per greedy step, the selected ids compacted into LDS and
+//     the index list written position-parallel (coalesced).
+//   select_kernel       1024 threads, any C: scores in registers up to
+//     16384 chunks, else re-read from memory; one exclusive scan per tile
+//     of 1024 chunks places every kept token.
 #include "chunkkv_internal.h"
 
 namespace ckv {
@@ -187,9 +197,208 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
   if (tid == 0) P.lengths[li * P.len_layer_stride + P.len_off[b] + h] = carry_off;
 }
 
+
+// ------------------------------------------------------------ fast path --
+constexpr int kFastThreads = 256;
+constexpr int kFastWaves = kFastThreads / 64;
+constexpr int kFastMaxKPT = 32;
+constexpr int kFastMaxChunks = kFastThreads * kFastMaxKPT;
+constexpr int kFastTable = kFastMaxKPT * kFastWaves;
+
+__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
+
+// Lanes below this one with their bit set in `mask`.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
+}
+
+// Exclusive prefix sum, in place, of tab[0 .. E) (E <= 128) by wave 0;
+// tab[E] receives the total.  Callers barrier before and after.
+__device__ __forceinline__ void wave0_scan_table(int* tab, int E) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int e0 = 2 * lane;
+  const int a = e0 < E ? tab[e0] : 0, b = e0 + 1 < E ? tab[e0 + 1] : 0;
+  int x = a + b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  const int base = x - a - b;
+  if (e0 < E) tab[e0] = base;
+  if (e0 + 1 < E) tab[e0 + 1] = base + a;
+  if (lane == 63) tab[E] = x;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectParams P) {
+  extern __shared__ int sel_ids[];                  // selected chunk ids < j_w, ascending
+  __shared__ int4 red[2][kFastWaves];
+  __shared__ int eq_tab[kFastTable + 1];
+  __shared__ int sel_tab[kFastTable + 1];
+  __shared__ int jw_selected;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  constexpr int E = KPT * kFastWaves;               // (slot, wave) table entries
+
+  const int per_layer = P.n_seqs * P.H_kv;
+  const int li = blockIdx.x / per_layer;
+  const int rest = blockIdx.x - li * per_layer;
+  const int b = rest / P.H_kv, h = rest - b * P.H_kv;
+  const int T = P.T[b], C = P.C[b], c = P.c, w = P.w;
+  const int kk = min(P.kk[b], C);
+  const unsigned* Sb = reinterpret_cast<const unsigned*>(P.scores + li * P.score_layer_stride +
+                                                         P.score_off[b] + static_cast<int64_t>(h) * C);
+  int32_t* idx = P.indices + li * P.index_layer_stride + P.index_off[b] + static_cast<int64_t>(h) * P.L_cap[b];
+
+  unsigned key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int j = i * kFastThreads + tid;
+    key[i] = j < C ? Sb[j] : 0u;   // padding 0 is below every candidate (>= 1)
+  }
+
+  // greedy threshold; n_ge tracks #{j < C : S_j >= tau}
+  unsigned tau = 0;
+  int n_ge = C;
+  int buf = 0;
+  auto wg_sum = [&](int4 v) {
+    red[buf][wave] = v;
+    __syncthreads();
+    int4 t = red[buf][0];
+#pragma unroll
+    for (int q = 1; q < kFastWaves; ++q) {
+      const int4 u = red[buf][q];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+    }
+    buf ^= 1;   // the next sum writes the other buffer: no second barrier
+    return t;
+  };
+  if (kk > 0 && kk < C) {
+    {
+      const unsigned c1 = 1u << 30;
+      int n1 = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) n1 += wave_count(key[i] >= c1);
+      const int4 t = wg_sum(make_int4(n1, 0, 0, 0));
+      if (t.x >= kk) {
+        tau = c1;
+        n_ge = t.x;
+      }
+    }
+    for (int bit = 28; bit >= 0; bit -= 2) {
+      const unsigned c1 = tau | (1u << bit), c2 = tau | (2u << bit), c3 = tau | (3u << bit);
+      int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        n1 += wave_count(key[i] >= c1);
+        n2 += wave_count(key[i] >= c2);
+        n3 += wave_count(key[i] >= c3);
+      }
+      const int4 t = wg_sum(make_int4(n1, n2, n3, 0));
+      if (t.z >= kk) {
+        tau = c3;
+        n_ge = t.z;
+      } else if (t.y >= kk) {
+        tau = c2;
+        n_ge = t.y;
+      } else if (t.x >= kk) {
+        tau = c1;
+        n_ge = t.x;
+      }
+    }
+  }
+
+  // ties: only when more than k chunks reach tau are the equal ones ranked
+  const bool all = kk >= C, none = kk == 0;
+  const bool ranked = !all && !none && n_ge > kk;
+  int need = 0;
+  if (ranked) {
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = i * kFastThreads + tid;
+      const unsigned long long m = __ballot(j < C && key[i] == tau);
+      gt += wave_count(key[i] > tau);
+      eq_tab[i * kFastWaves + wave] = __popcll(m);
+    }
+    const int4 t = wg_sum(make_int4(gt, 0, 0, 0));   // its barrier also publishes eq_tab
+    need = kk - t.x;
+    wave0_scan_table(eq_tab, E);
+    __syncthreads();
+  }
+
+  const int j_w = (T - w) / c;
+  unsigned long long pre[KPT];   // per slot: wave mask of selected chunks before j_w
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int j = i * kFastThreads + tid;
+    bool sel;
+    if (j >= C || none) {
+      sel = false;
+    } else if (all) {
+      sel = true;
+    } else if (!ranked) {
+      sel = key[i] >= tau;
+    } else {
+      const bool eq = key[i] == tau;
+      const unsigned long long m = __ballot(eq);
+      sel = key[i] > tau || (eq && eq_tab[i * kFastWaves + wave] + lanes_below(m) < need);
+    }
+    if (j == j_w) jw_selected = sel ? 1 : 0;
+    pre[i] = __ballot(sel && j < j_w);
+    sel_tab[i * kFastWaves + wave] = __popcll(pre[i]);
+  }
+  __syncthreads();
+  wave0_scan_table(sel_tab, E);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if ((pre[i] >> (tid & 63)) & 1ull)
+      sel_ids[sel_tab[i * kFastWaves + wave] + lanes_below(pre[i])] = i * kFastThreads + tid;
+  }
+  __syncthreads();
+
+  const int m = sel_tab[E];
+  const int tail0 = jw_selected ? j_w * c : T - w;
+  const int head = m * c;
+  const int n = head + (T - tail0);
+  for (int p = tid; p < n; p += kFastThreads) {
+    int tok;
+    if (p < head) {
+      const int q = p / c;
+      tok = sel_ids[q] * c + (p - q * c);
+    } else {
+      tok = tail0 + (p - head);
+    }
+    idx[p] = tok;
+  }
+  if (tid == 0) P.lengths[li * P.len_layer_stride + P.len_off[b] + h] = n;
+}
+
+template <int KPT>
+hipError_t launch_fast(const SelectParams& p, int n_blocks, int c_max, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(c_max) * sizeof(int);
+  hipLaunchKernelGGL(select_fast_kernel<KPT>, dim3(n_blocks), dim3(kFastThreads), lds, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s) {
+  int c_max = 1;
+  for (int b = 0; b < p.n_seqs; ++b) c_max = p.C[b] > c_max ? p.C[b] : c_max;
+  if (c_max <= kFastMaxChunks) {
+    if (c_max <= 1 * kFastThreads) return launch_fast<1>(p, n_blocks, c_max, s);
+    if (c_max <= 2 * kFastThreads) return launch_fast<2>(p, n_blocks, c_max, s);
+    if (c_max <= 4 * kFastThreads) return launch_fast<4>(p, n_blocks, c_max, s);
+    if (c_max <= 8 * kFastThreads) return launch_fast<8>(p, n_blocks, c_max, s);
+    if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, c_max, s);
+    return launch_fast<32>(p, n_blocks, c_max, s);
+  }
   hipLaunchKernelGGL(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
   return hipGetLastError();
 }

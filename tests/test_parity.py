@@ -107,6 +107,32 @@ def test_edge_cases(name, T, l_max, w, c):
         assert np.all(n == w)
 
 
+@pytest.mark.parametrize("dtype,d,c,T", [(ck.BF16, 128, 10, 3001), (ck.BF16, 128, 1, 2500),
+                                         (ck.F32, 64, 10, 1201), (ck.BF16, 128, 2, 9001)])
+def test_tied_scores_lower_id_first(dtype, d, c, T):
+    # all-zero keys: every logit is 0, so every full chunk gets the same score
+    # (c/T per row) and only the short last chunk differs; the top-k must take
+    # the lowest chunk ids (ChunkKV page, section 4.1: ties are broken towards
+    # the lower chunk id).
+    l_max = T // 5
+    case = random_case(dtype, [T], [l_max], 8, 2, d, 16, c, seed=T, scale_k=0.0).run()
+    _all_units(case)
+    kk = l_max // c
+    for h in range(2):
+        idx, _ = case.gpu_indices(0, 0, h)
+        assert np.array_equal(idx[:kk * c], np.arange(kk * c))
+
+
+def test_scores_underflow_to_zero():
+    # very peaked attention: most chunk scores are exactly 0 in fp32 and the
+    # k-th largest is 0, so the selection breaks a tie among the zero chunks.
+    case = random_case(ck.BF16, [5000], [2000], 8, 2, 128, 16, 2, seed=5, scale_k=300.0).run()
+    _all_units(case)
+    for h in range(2):
+        s = case.gpu_scores(0, 0, h)
+        assert np.count_nonzero(s) < 1000 < s.size
+
+
 def test_ragged_batch_and_many_sequences():
     # independent sequences packed along the token axis, each with its own
     # T_b and L_max,b; 11 sequences force several launches per phase.
