@@ -108,7 +108,10 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   pl.w = p->window;
   pl.c = p->chunk;
   pl.R = static_cast<int>(R);
-  pl.mfma = p->dtype == CHUNKKV_BF16 && p->head_dim == 128 && score_mfma_supported(p->chunk);
+  // the MFMA kernel addresses the keys of a group (at most 128 token rows)
+  // with 32-bit byte offsets
+  pl.mfma = p->dtype == CHUNKKV_BF16 && p->head_dim == 128 && score_mfma_supported(p->chunk) &&
+            p->kv_stride_tok * 2 * 128 < (int64_t{1} << 31);
   pl.R_pad = static_cast<int>(pl.mfma ? round_up(R, kMfmaRows) : round_up(R, 4));
   pl.n_rb = pl.mfma ? pl.R_pad / kMfmaRows : 1;
   pl.span_chunks = pl.mfma ? score_mfma_span_chunks(pl.c) : score_generic_span_chunks(pl.R_pad, pl.c);

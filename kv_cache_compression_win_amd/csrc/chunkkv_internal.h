@@ -15,7 +15,7 @@ constexpr int kMaxSeqs = 8;
 constexpr int kThreads = 256;            // every kernel: 4 wave64s per workgroup
 constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score workgroup
 #ifndef CKV_GATHER_ROWS
-#define CKV_GATHER_ROWS 64
+#define CKV_GATHER_ROWS 32
 #endif
 #ifndef CKV_SPAN_TARGET
 #define CKV_SPAN_TARGET 64
@@ -25,6 +25,15 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #endif
 #ifndef CKV_STAGE_TILES
 #define CKV_STAGE_TILES 8
+#endif
+#ifndef CKV_KBUF
+#define CKV_KBUF 1
+#endif
+// Cache policy of the score kernel's key loads (buffer instruction aux bits;
+// 2 = non-temporal: keys are read once, so they should not displace the chunk
+// partials and window queries in L2).
+#ifndef CKV_KAUX
+#define CKV_KAUX 2
 #endif
 #ifndef CKV_MIN_WAVES
 #define CKV_MIN_WAVES 2

@@ -14,7 +14,10 @@ namespace ckv {
 namespace {
 
 #ifndef CKV_GATHER_UNROLL
-#define CKV_GATHER_UNROLL 4
+#define CKV_GATHER_UNROLL 2
+#endif
+#ifndef CKV_GATHER_NT
+#define CKV_GATHER_NT 1
 #endif
 constexpr int kUnroll = CKV_GATHER_UNROLL;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -54,8 +57,13 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) 
       if (u < total) {
         const int i = u / upr, p = u - i * upr;
         const int64_t src = static_cast<int64_t>(idx[i]) * P.kv_st_bytes + p * 16;
+#if CKV_GATHER_NT
+        kv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + src));
+        vv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + src));
+#else
         kv[x] = *reinterpret_cast<const u32x4*>(ks + src);
         vv[x] = *reinterpret_cast<const u32x4*>(vs + src);
+#endif
         dst[x] = static_cast<int64_t>(i) * P.row_bytes + p * 16;
       }
     }

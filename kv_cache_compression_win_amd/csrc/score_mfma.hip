@@ -29,6 +29,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 
 constexpr int kD = 128;              // head_dim of this path
+// Buffer resource word 3 for raw dword loads on gfx9-family (CDNA) parts.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
@@ -106,9 +108,9 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
   float* dst = u_row + gi * G::GROUP_CHUNKS * kMfmaRows;
 #pragma unroll
   for (int q = 0; q < G::CPH; ++q) {
-    float u = 0.0f;
+    float u = __builtin_amdgcn_exp2f(fmaf(acc[(q * CC) >> 4][(q * CC) & 15], scale, -mrs));
 #pragma unroll
-    for (int e = 0; e < CC; ++e) {
+    for (int e = 1; e < CC; ++e) {
       const int lam = q * CC + e;
       u += __builtin_amdgcn_exp2f(fmaf(acc[lam >> 4][lam & 15], scale, -mrs));
     }
@@ -120,7 +122,17 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
 // One work item: (layer, sequence, KV head, row block, span of whole chunks).
 struct Item {
   int li, b, h, rb, span, nspan, C, tok_begin, tok_end, ngroups;
+  uint64_t kbase;   // byte address of token 0 of this sequence, head h
 };
+
+// Values read from the LDS tables are the same in every lane; moving them to
+// scalar registers keeps the address and cursor arithmetic on the scalar unit.
+__device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t sgpr64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 // The launch's per-layer and per-sequence tables, copied to LDS once so that
 // decoding an item with a runtime index never issues a vector memory load
@@ -169,18 +181,21 @@ __device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& 
   it.li = flat / P.items_per_layer;
   int item = flat - it.li * P.items_per_layer;
   int b = 0;
-  while (b + 1 < P.n_seqs && item >= t.item0[b + 1]) ++b;
-  item -= t.item0[b];
+  while (b + 1 < P.n_seqs && item >= sgpr(t.item0[b + 1])) ++b;
+  item -= sgpr(t.item0[b]);
   it.b = b;
-  it.nspan = t.n_span[b];
+  it.nspan = sgpr(t.n_span[b]);
   it.span = item % it.nspan;
   const int hr = item / it.nspan;
   it.rb = hr % P.n_rb;
   it.h = hr / P.n_rb;
-  it.C = t.C[b];
+  it.C = sgpr(t.C[b]);
   it.tok_begin = it.span * G::SPAN_CHUNKS * CC;
-  it.tok_end = min(t.T[b], it.tok_begin + G::SPAN_CHUNKS * CC);
+  it.tok_end = min(sgpr(t.T[b]), it.tok_begin + G::SPAN_CHUNKS * CC);
   it.ngroups = (it.tok_end - it.tok_begin + G::GROUP_TOK - 1) / G::GROUP_TOK;
+  it.kbase = sgpr64(t.k[it.li]) +
+             2 * static_cast<uint64_t>(static_cast<int64_t>(sgpr64(t.tok0[b])) * P.kv_st +
+                                       static_cast<int64_t>(it.h) * P.kv_sh);
   return it;
 }
 
@@ -210,7 +225,10 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 template <int CC>
 __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
-  __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
+  // CKV_KBUF key buffers: with two, group k is stored into buffer k % 2 and
+  // one barrier per group suffices (the buffer written next was last read
+  // before the previous barrier)
+  __shared__ u32x4 k_lds_all[CKV_KBUF][G::NT * 32 * kPieces];
   __shared__ float u_lds[G::SPAN_CHUNKS * kMfmaRows];
   __shared__ Tables tab;
 
@@ -252,27 +270,31 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   };
 
   // key streaming: slot (tile tau, row i) <-> token of lane half (i/4)%2.
-  // Every slot is loaded unconditionally: rows past the end of the span are
-  // clamped to its last row and padding slots (lam >= HALF_TOK) to the half's
-  // last slot, so their requests coincide with real ones; their logits are
-  // never used (padding) or masked (past the end).
+  // Keys are read through a buffer resource whose base is the group's first
+  // token and whose size ends at the span's end, so each lane's offsets are
+  // fixed for the whole kernel and tokens past the end of the sequence read
+  // as zeros (their logits are masked).  Padding slots (lam >= HALF_TOK)
+  // repeat the half's last slot; their logits are never used.
   u32x4 regs[G::STAGES][G::LOADS];
-  const int64_t st_bytes = P.kv_st * 2;
-  auto load_group = [&](u32x4 (&dst)[G::LOADS], const Item& it, int gi) {
-    const uint64_t kbase = tab.k[it.li] + 2 * static_cast<uint64_t>(tab.tok0[it.b] * P.kv_st +
-                                                                    static_cast<int64_t>(it.h) * P.kv_sh);
-    const int gtok0 = it.tok_begin + gi * G::GROUP_TOK;
+  const int st_bytes = static_cast<int>(P.kv_st * 2);   // < 2^31 / 128, checked on the host
+  int voff[G::LOADS];
 #pragma unroll
-    for (int x = 0; x < G::LOADS; ++x) {
-      const int gp = x * kThreads + tid;
-      const int sr = gp / kPieces, p = gp % kPieces;
-      const int tau = sr >> 5, i = sr & 31;
-      const int lam = min(16 * tau + 4 * (i >> 3) + (i & 3), G::HALF_TOK - 1);
-      const int tok = min(gtok0 + ((i >> 2) & 1) * G::HALF_TOK + lam, it.tok_end - 1);
-      dst[x] = *((gu32x4*)(kbase + tok * st_bytes + p * 16));
-    }
+  for (int x = 0; x < G::LOADS; ++x) {
+    const int gp = x * kThreads + tid;
+    const int sr = gp / kPieces, p = gp % kPieces;
+    const int tau = sr >> 5, i = sr & 31;
+    const int lam = min(16 * tau + 4 * (i >> 3) + (i & 3), G::HALF_TOK - 1);
+    voff[x] = (((i >> 2) & 1) * G::HALF_TOK + lam) * st_bytes + p * 16;
+  }
+  auto load_group = [&](u32x4 (&dst)[G::LOADS], const Item& it, int gi) {
+    const int gtok0 = it.tok_begin + gi * G::GROUP_TOK;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(it.kbase + static_cast<uint64_t>(gtok0) * st_bytes), 0,
+        min(it.tok_end - gtok0, G::GROUP_TOK) * st_bytes, kBufferWord3);
+#pragma unroll
+    for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, CKV_KAUX);
   };
-  auto store_group = [&](const u32x4 (&src)[G::LOADS]) {
+  auto store_group = [&](const u32x4 (&src)[G::LOADS], u32x4* k_lds) {
 #pragma unroll
     for (int x = 0; x < G::LOADS; ++x) {
       const int gp = x * kThreads + tid;
@@ -318,13 +340,16 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     __builtin_amdgcn_sched_barrier(0);
   }
   float m_ref = -INFINITY, l_acc = 0.0f;
+  int kbuf = 0;
 
   // one group of the stream, held in ring stage S; false when the range ends
   auto step = [&](auto stage_tag) -> bool {
     constexpr int S = decltype(stage_tag)::value;
-    __syncthreads();  // previous group's LDS reads (and any flush) are done
-    store_group(regs[S]);
+    u32x4* k_lds = k_lds_all[kbuf];
+    if constexpr (CKV_KBUF == 1) __syncthreads();  // previous group's LDS reads (and any flush) are done
+    store_group(regs[S], k_lds);
     __syncthreads();
+    if constexpr (CKV_KBUF > 1) kbuf = kbuf + 1 == CKV_KBUF ? 0 : kbuf + 1;
     load_next(regs[S]);
     f32x16 acc[G::NT];
 #pragma unroll
