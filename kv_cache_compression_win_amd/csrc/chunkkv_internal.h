@@ -24,7 +24,7 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #define CKV_MAX_TILES 4
 #endif
 #ifndef CKV_STAGE_TILES
-#define CKV_STAGE_TILES 8
+#define CKV_STAGE_TILES 4
 #endif
 #ifndef CKV_KBUF
 #define CKV_KBUF 1

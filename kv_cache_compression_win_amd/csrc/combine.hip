@@ -16,8 +16,11 @@
 namespace ckv {
 namespace {
 
+#ifndef CKV_COMBINE_SPANS
+#define CKV_COMBINE_SPANS 4
+#endif
 constexpr int kMaxRows = 4096;
-constexpr int kWeightFloats = 4096;   // weights of one item's spans (16 KB)
+constexpr int kWeightFloats = 16384;  // weights of one item's spans (64 KB at most)
 
 template <int QPT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
@@ -60,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
 }  // namespace
 
 int combine_spans_per_blk(int R_pad) {
-  const int spb = kWeightFloats / R_pad;
-  return spb < 1 ? 1 : (spb > 4 ? 4 : spb);
+  const int spb = 4096 / R_pad;
+  return spb < 1 ? 1 : (spb > CKV_COMBINE_SPANS ? CKV_COMBINE_SPANS : spb);
 }
 
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {

@@ -71,10 +71,31 @@ struct Geo {
 
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
-// Softmax pieces of one group for this lane's row: rebase the reference if the
-// group's maximum exceeds it by more than 2^kRebaseLog2, then write the chunk
-// partials of this lane half to LDS.  Slots past the end of the sequence are
-// masked to -inf (exp2 gives 0) before anything else.
+// Sum of the exponentials of one chunk's logits (terms q*CC .. q*CC+CC-1 of
+// the lane half), as a balanced tree: short dependency chains.
+template <int CC>
+__device__ __forceinline__ float chunk_exp_sum(const f32x16 (&acc)[Geo<CC>::NT], int q, float scale, float nmrs) {
+  float t[CC];
+#pragma unroll
+  for (int e = 0; e < CC; ++e) {
+    const int lam = q * CC + e;
+    t[e] = __builtin_amdgcn_exp2f(fmaf(acc[lam >> 4][lam & 15], scale, nmrs));
+  }
+#pragma unroll
+  for (int w = 1; w < CC; w *= 2)
+#pragma unroll
+    for (int e = 0; e + w < CC; e += 2 * w) t[e] += t[e + w];
+  return t[0];
+}
+
+// Softmax pieces of one group for this lane's row: write the chunk partials
+// of this lane half to LDS, relative to the row's reference m_ref.  The
+// reference is moved (and the earlier partials and l rescaled) only when the
+// group's maximum exceeds it by more than 2^kRebaseLog2.  That test needs the
+// group maximum, so it is made only when some lane's chunk sum reaches 2^63
+// or is not finite (always the case on a span's first group, where m_ref is
+// -inf): without it, every term is below 2^64 and the test would fail anyway.
+// Slots past the end of the sequence are masked to -inf (exp2 gives 0).
 template <int CC>
 __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool full, int nvalid,
                                               float scale, float rebase_raw, float& m_ref,
@@ -89,33 +110,37 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
         if (lam < G::HALF_TOK) acc[tau][v] = lam < nvalid ? acc[tau][v] : -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  float u[G::CPH];
+  bool ok = true;
 #pragma unroll
-  for (int tau = 0; tau < G::NT; ++tau)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (16 * tau + v < G::HALF_TOK) mx = fmaxf(mx, acc[tau][v]);
-  mx = fmaxf(mx, shfl_xor32(mx));
-  if (mx > m_ref + rebase_raw) {
-    const float f = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mx) * scale);
-    for (int gg = 0; gg < gi; ++gg)
-#pragma unroll
-      for (int q = 0; q < G::CPH; ++q) u_row[(gg * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
-    l_acc *= f;
-    m_ref = mx;
+  for (int q = 0; q < G::CPH; ++q) {
+    u[q] = chunk_exp_sum<CC>(acc, q, scale, -m_ref * scale);
+    ok = ok && (u[q] < 0x1p63f);   // false for +inf and NaN too
   }
-  const float mrs = m_ref * scale;
+  if (__ballot(!ok) != 0) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < G::NT; ++tau)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (16 * tau + v < G::HALF_TOK) mx = fmaxf(mx, acc[tau][v]);
+    mx = fmaxf(mx, shfl_xor32(mx));
+    if (mx > m_ref + rebase_raw) {
+      const float f = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mx) * scale);
+      for (int gg = 0; gg < gi; ++gg)
+#pragma unroll
+        for (int q = 0; q < G::CPH; ++q) u_row[(gg * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
+      l_acc *= f;
+      m_ref = mx;
+#pragma unroll
+      for (int q = 0; q < G::CPH; ++q) u[q] = chunk_exp_sum<CC>(acc, q, scale, -m_ref * scale);
+    }
+  }
   float* dst = u_row + gi * G::GROUP_CHUNKS * kMfmaRows;
 #pragma unroll
   for (int q = 0; q < G::CPH; ++q) {
-    float u = __builtin_amdgcn_exp2f(fmaf(acc[(q * CC) >> 4][(q * CC) & 15], scale, -mrs));
-#pragma unroll
-    for (int e = 1; e < CC; ++e) {
-      const int lam = q * CC + e;
-      u += __builtin_amdgcn_exp2f(fmaf(acc[lam >> 4][lam & 15], scale, -mrs));
-    }
-    dst[q * kMfmaRows] = u;
-    l_acc += u;
+    dst[q * kMfmaRows] = u[q];
+    l_acc += u[q];
   }
 }
 
