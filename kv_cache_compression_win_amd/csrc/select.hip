@@ -199,9 +199,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
 
 
 // ------------------------------------------------------------ fast path --
-constexpr int kFastThreads = 256;
+#ifndef CKV_SELECT_THREADS
+#define CKV_SELECT_THREADS 512
+#endif
+constexpr int kFastThreads = CKV_SELECT_THREADS;
 constexpr int kFastWaves = kFastThreads / 64;
-constexpr int kFastMaxKPT = 32;
+constexpr int kFastMaxKPT = 128 / kFastWaves;   // (slot, wave) tables of at most 128 entries
 constexpr int kFastMaxChunks = kFastThreads * kFastMaxKPT;
 constexpr int kFastTable = kFastMaxKPT * kFastWaves;
 
@@ -395,9 +398,11 @@ hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s) {
     if (c_max <= 1 * kFastThreads) return launch_fast<1>(p, n_blocks, c_max, s);
     if (c_max <= 2 * kFastThreads) return launch_fast<2>(p, n_blocks, c_max, s);
     if (c_max <= 4 * kFastThreads) return launch_fast<4>(p, n_blocks, c_max, s);
-    if (c_max <= 8 * kFastThreads) return launch_fast<8>(p, n_blocks, c_max, s);
-    if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, c_max, s);
-    return launch_fast<32>(p, n_blocks, c_max, s);
+    if constexpr (kFastMaxKPT >= 8)
+      if (c_max <= 8 * kFastThreads) return launch_fast<8>(p, n_blocks, c_max, s);
+    if constexpr (kFastMaxKPT >= 16)
+      if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, c_max, s);
+    if constexpr (kFastMaxKPT >= 32) return launch_fast<32>(p, n_blocks, c_max, s);
   }
   hipLaunchKernelGGL(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
   return hipGetLastError();
