@@ -26,9 +26,6 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #ifndef CKV_STAGE_TILES
 #define CKV_STAGE_TILES 4
 #endif
-#ifndef CKV_KBUF
-#define CKV_KBUF 1
-#endif
 // Cache policy of the score kernel's key loads (buffer instruction aux bits;
 // 2 = non-temporal: keys are read once, so they should not displace the chunk
 // partials and window queries in L2).

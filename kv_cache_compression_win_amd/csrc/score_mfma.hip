@@ -250,10 +250,7 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 template <int CC>
 __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
-  // CKV_KBUF key buffers: with two, group k is stored into buffer k % 2 and
-  // one barrier per group suffices (the buffer written next was last read
-  // before the previous barrier)
-  __shared__ u32x4 k_lds_all[CKV_KBUF][G::NT * 32 * kPieces];
+  __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
   __shared__ float u_lds[G::SPAN_CHUNKS * kMfmaRows];
   __shared__ Tables tab;
 
@@ -319,7 +316,7 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
 #pragma unroll
     for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, CKV_KAUX);
   };
-  auto store_group = [&](const u32x4 (&src)[G::LOADS], u32x4* k_lds) {
+  auto store_group = [&](const u32x4 (&src)[G::LOADS]) {
 #pragma unroll
     for (int x = 0; x < G::LOADS; ++x) {
       const int gp = x * kThreads + tid;
@@ -327,21 +324,39 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
       k_lds[sr * kPieces + (p ^ (sr & 15))] = src[x];
     }
   };
-  // per-row span statistics and chunk partials of a finished item
+  // Per-row span statistics and chunk partials of a finished item.  The
+  // stores go through buffer resources sized to the data (pieces past the
+  // span's last chunk are dropped), so their number is fixed: the compiler's
+  // memory-counter waits in the main loop then stay exact.
   auto flush = [&](const Item& it, float m_ref, float l_acc) {
-    const int r = it.rb * kMfmaRows + wave * 32 + n;
     const float l_row = l_acc + shfl_xor32(l_acc);
-    if (ho == 0 && r < P.R)
-      P.stats[it.li * P.st_layer_stride + tab.st_off[it.b] +
-              (static_cast<int64_t>(it.h) * it.nspan + it.span) * P.R_pad + r] = make_float2(m_ref, l_row);
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const uint64_t sbase = reinterpret_cast<uint64_t>(P.stats + it.li * P.st_layer_stride) +
+                           8 * static_cast<uint64_t>(sgpr64(tab.st_off[it.b]) +
+                                                     (static_cast<int64_t>(it.h) * it.nspan + it.span) * P.R_pad +
+                                                     it.rb * kMfmaRows);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(sgpr64(sbase)), 0, kMfmaRows * 8, kBufferWord3);
+    // both lane halves hold the row's statistics; half 1 aims past the end
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_ref), __float_as_uint(l_row)}, rs,
+                                          (wave * 32 + n) * 8 + ho * kMfmaRows * 8, 0, 0);
     __syncthreads();
-    const int nch = min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS);
-    float* ug = P.U + it.li * P.u_layer_stride + tab.u_off[it.b] +
-                (static_cast<int64_t>(it.h) * it.C + it.span * G::SPAN_CHUNKS) * P.R_pad + it.rb * kMfmaRows;
-    for (int e = tid; e < nch * (kMfmaRows / 4); e += kThreads) {
+    const int nch = sgpr(min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS));
+    const uint64_t ubase = reinterpret_cast<uint64_t>(P.U + it.li * P.u_layer_stride) +
+                           4 * static_cast<uint64_t>(sgpr64(tab.u_off[it.b]) +
+                                                     (static_cast<int64_t>(it.h) * it.C + it.span * G::SPAN_CHUNKS) *
+                                                         P.R_pad +
+                                                     it.rb * kMfmaRows);
+    const int chunk_bytes = P.R_pad * 4;
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(sgpr64(ubase)), 0, nch * chunk_bytes, kBufferWord3);
+    constexpr int kPieces4 = G::SPAN_CHUNKS * (kMfmaRows / 4);
+#pragma unroll
+    for (int x = 0; x < (kPieces4 + kThreads - 1) / kThreads; ++x) {
+      const int e = x * kThreads + tid;
       const int j = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
-      const float4 val = *reinterpret_cast<const float4*>(&u_lds[j * kMfmaRows + c4 * 4]);
-      *reinterpret_cast<float4*>(ug + static_cast<int64_t>(j) * P.R_pad + c4 * 4) = val;
+      const u32x4 val = reinterpret_cast<const u32x4*>(u_lds)[min(e, kPieces4 - 1)];
+      __builtin_amdgcn_raw_buffer_store_b128(val, ru, j * chunk_bytes + c4 * 16, 0, 0);
     }
   };
 
@@ -365,45 +380,56 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     __builtin_amdgcn_sched_barrier(0);
   }
   float m_ref = -INFINITY, l_acc = 0.0f;
-  int kbuf = 0;
 
-  // one group of the stream, held in ring stage S; false when the range ends
-  auto step = [&](auto stage_tag) -> bool {
+  // total key groups of this workgroup's range: the main loop is counted, so
+  // its only branches are uniform ones around the compute and write-back
+  int total = 0;
+  for (int f = lo; f < hi; ++f) total += decode_item<CC>(P, tab, f).ngroups;
+
+  // one group of the stream, held in ring stage S; steps past the end of the
+  // range (live == false) still issue their loads (repeats of the last group)
+  auto step = [&](auto stage_tag, bool live) {
     constexpr int S = decltype(stage_tag)::value;
-    u32x4* k_lds = k_lds_all[kbuf];
-    if constexpr (CKV_KBUF == 1) __syncthreads();  // previous group's LDS reads (and any flush) are done
-    store_group(regs[S], k_lds);
+    __syncthreads();  // previous group's LDS reads (and any flush) are done
+    store_group(regs[S]);
     __syncthreads();
-    if constexpr (CKV_KBUF > 1) kbuf = kbuf + 1 == CKV_KBUF ? 0 : kbuf + 1;
     load_next(regs[S]);
-    f32x16 acc[G::NT];
+    if (live) {
+      f32x16 acc[G::NT];
 #pragma unroll
-    for (int tau = 0; tau < G::NT; ++tau) {
-      acc[tau] = f32x16{};
+      for (int tau = 0; tau < G::NT; ++tau) {
+        acc[tau] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &k_lds[(tau * 32 + n) * kPieces + ((8 * ho + s) ^ (n & 15))]);
-        acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[tau], 0, 0, 0);
+        for (int s = 0; s < kKSteps; ++s) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &k_lds[(tau * 32 + n) * kPieces + ((8 * ho + s) ^ (n & 15))]);
+          acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[tau], 0, 0, 0);
+        }
       }
+      const Item& it = cc.it;
+      const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
+      const int nvalid = it.tok_end - (gtok0 + ho * G::HALF_TOK);
+      group_softmax<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, P.rebase_raw, m_ref, l_acc,
+                        u_row, cc.g);
+      if (cc.g + 1 == it.ngroups) {
+        flush(it, m_ref, l_acc);
+        m_ref = -INFINITY;
+        l_acc = 0.0f;
+      }
+      cursor_next<CC>(P, tab, cc, hi);
     }
-    const Item& it = cc.it;
-    const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
-    const int nvalid = it.tok_end - (gtok0 + ho * G::HALF_TOK);
-    group_softmax<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, P.rebase_raw, m_ref, l_acc,
-                      u_row, cc.g);
-    if (cc.g + 1 == it.ngroups) {
-      flush(it, m_ref, l_acc);
-      m_ref = -INFINITY;
-      l_acc = 0.0f;
-    }
-    return cursor_next<CC>(P, tab, cc, hi);
   };
-  for (;;) {
-    if (!step(std::integral_constant<int, 0>{})) break;
-    if constexpr (G::STAGES > 1) if (!step(std::integral_constant<int, 1 % G::STAGES>{})) break;
-    if constexpr (G::STAGES > 2) if (!step(std::integral_constant<int, 2 % G::STAGES>{})) break;
-    if constexpr (G::STAGES > 3) if (!step(std::integral_constant<int, 3 % G::STAGES>{})) break;
+  const int rounds = (total + G::STAGES - 1) / G::STAGES;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int k0 = rd * G::STAGES;
+    step(std::integral_constant<int, 0>{}, k0 < total);
+    if constexpr (G::STAGES > 1) step(std::integral_constant<int, 1 % G::STAGES>{}, k0 + 1 < total);
+    if constexpr (G::STAGES > 2) step(std::integral_constant<int, 2 % G::STAGES>{}, k0 + 2 < total);
+    if constexpr (G::STAGES > 3) step(std::integral_constant<int, 3 % G::STAGES>{}, k0 + 3 < total);
+    if constexpr (G::STAGES > 4) step(std::integral_constant<int, 4 % G::STAGES>{}, k0 + 4 < total);
+    if constexpr (G::STAGES > 5) step(std::integral_constant<int, 5 % G::STAGES>{}, k0 + 5 < total);
+    if constexpr (G::STAGES > 6) step(std::integral_constant<int, 6 % G::STAGES>{}, k0 + 6 < total);
+    if constexpr (G::STAGES > 7) step(std::integral_constant<int, 7 % G::STAGES>{}, k0 + 7 < total);
   }
 }
 
