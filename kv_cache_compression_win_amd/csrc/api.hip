@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Seq {
   int64_t tok0;
   int32_t T, C, kk, L_cap, n_span;
-  int64_t score_off, index_off, u_off, st_off;
+  int64_t score_off, index_off, u_off, st_off, lse_off;
 };
 
 struct Plan {
@@ -59,11 +59,12 @@ struct Plan {
   int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
   bool mfma = false;
   std::vector<Seq> seq;
-  int64_t scores_elems = 0, index_elems = 0, length_elems = 0, u_elems = 0, st_elems = 0;
+  int64_t scores_elems = 0, index_elems = 0, length_elems = 0, u_elems = 0, st_elems = 0, lse_elems = 0;
   int64_t kv_st = 0, kv_sh = 0, q_ss = 0, q_sr = 0, q_sh = 0;
   size_t ws_bytes(int n_layers) const {
     return align_up(static_cast<size_t>(n_layers) * u_elems * sizeof(float)) +
-           align_up(static_cast<size_t>(n_layers) * st_elems * sizeof(float2));
+           align_up(static_cast<size_t>(n_layers) * st_elems * sizeof(float2)) +
+           align_up(static_cast<size_t>(n_layers) * lse_elems * sizeof(float2));
   }
 };
 
@@ -142,10 +143,12 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     s.index_off = pl.index_elems;
     s.u_off = pl.u_elems;
     s.st_off = pl.st_elems;
+    s.lse_off = pl.lse_elems;
     pl.scores_elems += static_cast<int64_t>(pl.Hkv) * s.C;
     pl.index_elems += static_cast<int64_t>(pl.Hkv) * s.L_cap;
     pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * pl.R_pad;
     pl.st_elems += static_cast<int64_t>(pl.Hkv) * s.n_span * pl.R_pad;
+    pl.lse_elems += static_cast<int64_t>(pl.Hkv) * pl.R_pad;
     items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * s.n_span;
     pl.seq.push_back(s);
   }
@@ -211,7 +214,7 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
   return hipSuccess;
 }
 
-hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float* scores,
+hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
                        hipStream_t s) {
   const int spb = combine_spans_per_blk(pl.R_pad);
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
@@ -231,21 +234,28 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
       P.u_off[i] = sq.u_off;
       P.st_off[i] = sq.st_off;
       P.score_off[i] = sq.score_off;
+      P.lse_off[i] = sq.lse_off;
+      P.head0[i] = i * pl.Hkv;
       items += pl.Hkv * P.n_blk[i];
     }
     P.item0[nb] = items;
+    P.head0[nb] = nb * pl.Hkv;
     P.items_per_layer = items;
     P.u_layer_stride = pl.u_elems;
     P.st_layer_stride = pl.st_elems;
     P.score_layer_stride = pl.scores_elems;
+    P.lse_layer_stride = pl.lse_elems;
     P.U = U;
     P.stats = st;
+    P.lse = lse;
     P.scores = scores;
     P.H_kv = pl.Hkv;
     P.R = pl.R;
     P.R_pad = pl.R_pad;
     P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
-    const hipError_t e = launch_combine(P, nl * items, s);
+    hipError_t e = launch_row_lse(P, nl * nb * pl.Hkv, s);
+    if (e != hipSuccess) return e;
+    e = launch_combine(P, nl * items, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -326,10 +336,12 @@ hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* 
   return hipSuccess;
 }
 
-void carve(const Plan& pl, int nl, void* ws, float** U, float2** st) {
+void carve(const Plan& pl, int nl, void* ws, float** U, float2** st, float2** lse) {
+  const size_t u_bytes = align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float));
+  const size_t st_bytes = align_up(static_cast<size_t>(nl) * pl.st_elems * sizeof(float2));
   *U = static_cast<float*>(ws);
-  *st = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                  align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float)));
+  *st = reinterpret_cast<float2*>(static_cast<char*>(ws) + u_bytes);
+  *lse = reinterpret_cast<float2*>(static_cast<char*>(ws) + u_bytes + st_bytes);
 }
 
 int check_ws(const Plan& pl, const void* ws, size_t ws_bytes, int nl) {
@@ -381,11 +393,11 @@ int chunkkv_score(const chunkkv_problem* p, const void* q_win, const void* k, fl
   if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* U;
-  float2* st;
-  carve(pl, 1, workspace, &U, &st);
+  float2 *st, *lse;
+  carve(pl, 1, workspace, &U, &st, &lse);
   hipError_t e = run_score(pl, 1, &q_win, &k, U, st, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
-  e = run_combine(pl, 1, U, st, scores, s);
+  e = run_combine(pl, 1, U, st, lse, scores, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
@@ -456,8 +468,8 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
   if (e != hipSuccess) return hip_fail(e, "phase event");
 
   float* U;
-  float2* st;
-  carve(pl, batch, workspace, &U, &st);
+  float2 *st, *lse;
+  carve(pl, batch, workspace, &U, &st, &lse);
   const bool one_batch = n_anchor <= batch;
   const void* qb[kMaxLayers];
   const void* kb[kMaxLayers];
@@ -469,7 +481,7 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
     }
     if ((e = run_score(pl, na, qb, kb, U, st, s)) != hipSuccess) return hip_fail(e, "score launch");
     if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-    if ((e = run_combine(pl, na, U, st, scores + a0 * pl.scores_elems, s)) != hipSuccess)
+    if ((e = run_combine(pl, na, U, st, lse, scores + a0 * pl.scores_elems, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
     if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
                         lengths + a0 * pl.length_elems, s)) != hipSuccess)

@@ -101,9 +101,12 @@ struct CombineParams {
   int64_t u_off[kMaxSeqs];
   int64_t st_off[kMaxSeqs];
   int64_t score_off[kMaxSeqs];
-  int64_t u_layer_stride, st_layer_stride, score_layer_stride;
+  int64_t lse_off[kMaxSeqs];    // per-row (M, L) of sequence b: [H_kv][R_pad] float2
+  int32_t head0[kMaxSeqs + 1];  // first (sequence, head) item of sequence b in the row-statistics launch
+  int64_t u_layer_stride, st_layer_stride, score_layer_stride, lse_layer_stride;
   const float* U;
   const float2* stats;
+  float2* lse;
   float* scores;
   int32_t H_kv, R, R_pad;
   float scale;
@@ -170,6 +173,7 @@ size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d);
 hipError_t launch_score_generic(const ScoreParams& p, int dtype, int n_blocks, hipStream_t s);
 int combine_spans_per_blk(int R_pad);
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_row_lse(const CombineParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s);
 

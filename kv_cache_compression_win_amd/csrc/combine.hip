@@ -6,9 +6,10 @@
 //   M_r = max_s m_s,  L_r = sum_s 2^((m_s - M_r) * scale) * l_s,
 // and a chunk j of span s scores
 //   S_j = sum_r U[j][r] * 2^((m_s,r - M_r) * scale) / L_r.
-// Work item = (layer, sequence, KV head, block of spans): enough items to
-// fill the GPU.  Each item forms (M_r, L_r) itself from the statistics (a few
-// percent of the U bytes it reads) and then streams its chunks' U rows with
+// Two launches: row_lse_kernel forms (M_r, L_r) once per (layer, sequence,
+// KV head) from the span statistics; combine_kernel's work item is (layer,
+// sequence, KV head, block of spans), enough items to fill the GPU, each
+// reading the head's row statistics and streaming its chunks' U rows with
 // eight 16-byte loads in flight per thread.  The row sums follow the fixed
 // order of combine_chunks: results are deterministic.
 #include "lse_combine.h"
@@ -42,7 +43,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
 
   const float2* st = P.stats + li * P.st_layer_stride + P.st_off[b] +
                      static_cast<int64_t>(h) * nspan * P.R_pad;
-  rows_lse<kThreads>(st, nspan, P.R, P.R_pad, P.scale, lse);
+  const float2* lse_g = P.lse + li * P.lse_layer_stride + P.lse_off[b] + static_cast<int64_t>(h) * P.R_pad;
+  for (int r = tid; r < P.R; r += kThreads) lse[r] = lse_g[r];
   __syncthreads();
   const int s_lo = blk * P.spans_per_blk;
   const int ns = min(P.spans_per_blk, nspan - s_lo);
@@ -60,7 +62,28 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
   combine_chunks<kThreads, QPT>(U, wts, j_lo, j_hi, s_lo, P.span_chunks, P.R_pad, S);
 }
 
+// Row statistics of one (layer, sequence, KV head): (M_r, L_r) over all spans,
+// once per head for every combine block of the head.
+__global__ __launch_bounds__(kThreads) void row_lse_kernel(const CombineParams P) {
+  const int per_layer = P.head0[P.n_seqs];
+  const int li = blockIdx.x / per_layer;
+  const int item = blockIdx.x - li * per_layer;
+  int b = 0;
+  while (b + 1 < P.n_seqs && item >= P.head0[b + 1]) ++b;
+  const int h = item - P.head0[b];
+  const int nspan = P.n_span[b];
+  const float2* st = P.stats + li * P.st_layer_stride + P.st_off[b] +
+                     static_cast<int64_t>(h) * nspan * P.R_pad;
+  float2* lse_g = P.lse + li * P.lse_layer_stride + P.lse_off[b] + static_cast<int64_t>(h) * P.R_pad;
+  rows_lse<kThreads>(st, nspan, P.R, P.R_pad, P.scale, lse_g);
+}
+
 }  // namespace
+
+hipError_t launch_row_lse(const CombineParams& p, int n_blocks, hipStream_t s) {
+  hipLaunchKernelGGL(row_lse_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
 
 int combine_spans_per_blk(int R_pad) {
   const int spb = 4096 / R_pad;
