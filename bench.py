@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--workload", default="llama3-8b-32layer-T32768")
     ap.add_argument("--layers", type=int, default=None, help="use the first N layers only")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--context", choices=("on", "off"), default="on",
+                    help="after the timed steps, also time the 8-layer slice and a 1 GiB device copy")
     ap.add_argument("--cpu-anchor-pairs", type=int, default=2,
                     help="oracle sample: this many (scoring, reusing) layer pairs, all KV heads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -89,6 +91,24 @@ def copy_calibration(mib: int, reps: int = 5):
     ms = start.elapsed_time(stop) / reps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps, "ms": ms,
                       "copy_gbps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def copy_peak(n: int, start, stop, step_gbps: float, reps: int = 5):
+    """A plain 1 GiB device-to-device copy timed on the same stream: the
+    measured copy rate (read + write bytes) that the step is compared with."""
+    import torch
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n / (start.elapsed_time(stop) / reps * 1e-3) / 1e9
+    return {"gbps": gbps, "what": "1 GiB device-to-device copy (torch copy_), read + write bytes",
+            "step_hbm_frac": step_gbps / gbps}
 
 
 def cpu_baseline(wl, cache, n_pairs: int):
@@ -229,6 +249,28 @@ def main():
         "phases_ms": ph,
         "wall_s_timed": wall,
     }
+    # context outside the timed region: the 8-layer slice (its first 8
+    # layers: 4 scoring + 4 reusing) and a plain device copy of 1 GiB
+    extra = {}
+    if args.context == "on" and L > 8:
+        def slice8():
+            ck.compress_layers(prob, n_reuse, qs[:8], ks[:8], vs[:8], kos[:8], vos[:8], bufs.scores,
+                               bufs.indices, bufs.lengths, bufs.workspace, bufs.ws_bytes)
+        for _ in range(args.warmup):
+            slice8()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            slice8()
+        stop.record()
+        torch.cuda.synchronize()
+        ms8 = start.elapsed_time(stop) / args.steps
+        extra["slice_8_layers"] = {"ms_per_call": ms8, "value": 8 * sum(wl.seq_lens) / (ms8 * 1e-3),
+                                   "unit": "layer-tokens/s"}
+    n_copy = 1 << 30 if args.context == "on" else 0
+    if n_copy:
+        extra["copy_peak"] = copy_peak(n_copy, start, stop, step_gbps)
+    out.update(extra)
     if args.cpu_baseline == "on":
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, cache, args.cpu_anchor_pairs)
