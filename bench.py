@@ -153,8 +153,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: ChunkKV compression here has no multi-GPU path "
-              "(every (layer, sequence, KV head) unit is independent; see the sharding notes in "
-              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "(every (layer, sequence, KV head) unit is independent, so sequences, heads or "
+              "layers would be split across GPUs without any exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   CHUNKKV_OK = 0,
   CHUNKKV_ERR_INVALID_ARG = 1, /* a value outside the method's domain */
-  CHUNKKV_ERR_UNSUPPORTED = 2, /* valid for the method, not for this build */
+  CHUNKKV_ERR_UNSUPPORTED = 2, /* valid for the method, not supported by this library */
   CHUNKKV_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than planned */
   CHUNKKV_ERR_HIP = 4          /* a HIP runtime call failed */
 } chunkkv_status;
