@@ -150,8 +150,11 @@ int chunkkv_score(const chunkkv_problem *p, const void *q_win, const void *k, fl
  * is Kara eqs. (2)-(3)): per (sequence, KV head) select the floor(L_max/c)
  * top-scoring chunks (ties: lower chunk id), add the last w tokens, and write
  * the kept token positions (0-based within the sequence) in ascending order.
- *   scores   DEVICE fp32, as written by chunkkv_score (scores must be >= 0 and
- *            finite)
+ *   scores   DEVICE fp32, as written by chunkkv_score (>= 0).  Any other
+ *            values are accepted: a score with the sign bit set counts as 0
+ *            and the rest are ordered by their bit patterns (+inf above every
+ *            finite score), so exactly min(k, C) chunks are always selected
+ *            and every index lies in [0, T_b).
  *   indices  DEVICE int32 out, index_elems entries (entries i >= n untouched)
  *   lengths  DEVICE int32 out, length_elems entries
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.

@@ -31,6 +31,13 @@ namespace ckv {
 namespace {
 
 constexpr int kWaves = kSelectThreads / 64;
+
+// The key of a score: its fp32 bit pattern, whose unsigned order is the value
+// order for scores >= 0.  A pattern with the sign bit set (a negative score,
+// -0 or a negative NaN, none of which the score kernels produce) counts as 0,
+// so every pattern is below 2^31, the threshold search is exact and exactly
+// min(k, C) chunks are selected: the index list never exceeds L_cap.
+__device__ __forceinline__ unsigned score_key(unsigned pattern) { return (pattern >> 31) ? 0u : pattern; }
 constexpr int kKPT = kSelectKeysPerThread;
 
 // Workgroup-wide sum; every thread receives the total.
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
 #pragma unroll
   for (int i = 0; i < kKPT; ++i) {
     const int j = i * kSelectThreads + tid;
-    key[i] = (in_regs && j < C) ? Sb[j] : 0u;
+    key[i] = (in_regs && j < C) ? score_key(Sb[j]) : 0u;
   }
 
   unsigned tau = 0;
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
 #pragma unroll
         for (int i = 0; i < kKPT; ++i) cnt += key[i] >= cand ? 1 : 0;
       } else {
-        for (int j = tid; j < C; j += kSelectThreads) cnt += Sb[j] >= cand ? 1 : 0;
+        for (int j = tid; j < C; j += kSelectThreads) cnt += score_key(Sb[j]) >= cand ? 1 : 0;
       }
       return cnt;
     };
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
         }
       } else {
         for (int j = tid; j < C; j += kSelectThreads) {
-          const unsigned kj = Sb[j];
+          const unsigned kj = score_key(Sb[j]);
           cnt.x += kj >= c1 ? 1 : 0;
           cnt.y += kj >= c2 ? 1 : 0;
           cnt.z += kj >= c3 ? 1 : 0;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
 #pragma unroll
       for (int i = 0; i < kKPT; ++i) gt += key[i] > tau ? 1 : 0;
     } else {
-      for (int j = tid; j < C; j += kSelectThreads) gt += Sb[j] > tau ? 1 : 0;
+      for (int j = tid; j < C; j += kSelectThreads) gt += score_key(Sb[j]) > tau ? 1 : 0;
     }
     need = kk - block_sum(gt, red);
   }
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
   } else {
     for (int base = 0; base < C; base += kSelectThreads) {
       const int j = base + tid;
-      tile(j, j < C ? Sb[j] : 0u);
+      tile(j, j < C ? score_key(Sb[j]) : 0u);
     }
   }
   if (tid == 0) P.lengths[li * P.len_layer_stride + P.len_off[b] + h] = carry_off;
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int j = i * kFastThreads + tid;
-    key[i] = j < C ? Sb[j] : 0u;   // padding 0 is below every candidate (>= 1)
+    key[i] = j < C ? score_key(Sb[j]) : 0u;   // padding 0 is below every candidate (>= 1)
   }
 
   // greedy threshold; n_ge tracks #{j < C : S_j >= tau}

@@ -301,3 +301,53 @@ def test_llama70b_batch_sampled():
         s_ref = fut.result()
         for l in (a, a + 1):
             check_unit(case, l, b, h, s_ref=s_ref)
+
+
+# --------------------------------------------------- selection on any input --
+
+def _adversarial_scores(rng, C, with_pos_nan):
+    s = rng.random(C).astype(np.float32)
+    bits = s.view(np.uint32)
+    r = rng.random(C)
+    bits[r < 0.15] = np.float32(-1.5).view(np.uint32)      # negative
+    bits[(r >= 0.15) & (r < 0.25)] = 0x80000000             # -0
+    bits[(r >= 0.25) & (r < 0.32)] = 0xFFC00000             # negative NaN
+    bits[(r >= 0.32) & (r < 0.35)] = 0x7F800000             # +inf
+    if with_pos_nan:
+        bits[(r >= 0.35) & (r < 0.38)] = 0x7FC00000         # positive NaN
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("T,c,w,l_max", [(2000, 10, 16, 300),       # register path (C = 200)
+                                         (90001, 10, 32, 9000)])    # C = 9001 > 8192: 1024-thread kernel
+def test_select_any_scores_stays_in_range(T, c, w, l_max):
+    # chunkkv_select takes caller scores: a score with the sign bit set counts
+    # as 0 and the rest are ordered by bit pattern, so exactly k chunks are
+    # selected and the index list never leaves [0, T) or exceeds L_cap.
+    Hkv = 2
+    prob = ck.make_problem(ck.BF16, [T], [l_max], 4, Hkv, 128, w, c)
+    pl = ck.plan(prob)
+    C = -(-T // c)
+    kk = l_max // c
+    rng = np.random.default_rng(T)
+    for with_pos_nan in (False, True):
+        host = np.concatenate([_adversarial_scores(rng, C, with_pos_nan) for _ in range(Hkv)])
+        scores = torch.from_numpy(host).cuda()
+        indices = torch.full((pl["index_elems"],), POISON_INDEX, dtype=torch.int32, device="cuda")
+        lengths = torch.zeros(Hkv, dtype=torch.int32, device="cuda")
+        ck.select(prob, scores, indices, lengths)
+        torch.cuda.synchronize()
+        idx_all, n_all = indices.cpu().numpy(), lengths.cpu().numpy()
+        L_cap = int(pl["l_cap"][0])
+        for h in range(Hkv):
+            n = int(n_all[h])
+            idx = idx_all[h * L_cap:h * L_cap + n]
+            assert n <= L_cap
+            assert np.all(idx_all[h * L_cap + n:(h + 1) * L_cap] == POISON_INDEX)
+            assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < T
+            assert set(range(T - w, T)) <= set(idx.tolist())
+            if not with_pos_nan:
+                s = host[h * C:(h + 1) * C].astype(np.float64)
+                s = np.where(np.signbit(s), 0.0, s)            # sign bit -> 0
+                sel = oracle.topk(s, kk)
+                assert np.array_equal(idx, oracle.indices(T, w, c, sel))
