@@ -169,8 +169,10 @@ int chunkkv_select(const chunkkv_problem *p, const float *scores, int32_t *indic
  *   indices, lengths  DEVICE, as written by chunkkv_select (any layer's)
  *   k_out, v_out  DEVICE out, index_elems rows of head_dim elements each
  *                 (16-byte aligned); rows i >= n untouched
- * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Index values are trusted: each must
- * lie in [0, T_b).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Indices and lengths as written by
+ * chunkkv_select are always valid; other values are clamped (lengths into
+ * [0, L_cap_b], index values into [0, T_b)), so no input makes the copy read
+ * or write outside the sequence's rows and the head's output rows.
  */
 int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
                    const int32_t *indices, const int32_t *lengths, void *k_out, void *v_out,

@@ -314,6 +314,7 @@ hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* 
     for (int i = 0; i < nb; ++i) {
       const Seq& sq = pl.seq[b0 + i];
       P.tok0[i] = sq.tok0;
+      P.T[i] = sq.T;
       P.L_cap[i] = sq.L_cap;
       P.len_off[i] = (b0 + i) * pl.Hkv;
       P.item0[i] = items;

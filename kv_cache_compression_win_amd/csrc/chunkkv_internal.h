@@ -149,6 +149,7 @@ struct GatherParams {
   int32_t H_kv;
   int32_t items_per_layer;
   int64_t tok0[kMaxSeqs];
+  int32_t T[kMaxSeqs];
   int32_t L_cap[kMaxSeqs];
   int32_t len_off[kMaxSeqs];
   int32_t item0[kMaxSeqs + 1];

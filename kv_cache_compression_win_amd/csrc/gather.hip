@@ -32,7 +32,11 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) 
   const int bph = P.blocks_per_head[b];
   const int h = item / bph, blk = item - h * bph;
   const int blkL = P.idx_block[li];
-  const int n = P.lengths[blkL * P.len_layer_stride + P.len_off[b] + h];
+  // lengths and index values come from the selection (always in range); a
+  // caller's own are clamped, so no input reads or writes outside the
+  // sequence's rows and the head's L_cap output rows
+  const int n = min(max(P.lengths[blkL * P.len_layer_stride + P.len_off[b] + h], 0), P.L_cap[b]);
+  const int t_last = P.T[b] - 1;
   const int i0 = blk * kGatherRows;
   if (i0 >= n) return;
   const int nrows = min(kGatherRows, n - i0);
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) 
       dst[x] = -1;
       if (u < total) {
         const int i = u / upr, p = u - i * upr;
-        const int64_t src = static_cast<int64_t>(idx[i]) * P.kv_st_bytes + p * 16;
+        const int64_t src = static_cast<int64_t>(min(max(idx[i], 0), t_last)) * P.kv_st_bytes + p * 16;
 #if CKV_GATHER_NT
         kv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + src));
         vv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + src));

@@ -15,7 +15,7 @@ import torch
 
 import kvsynth
 import oracle
-from harness import (ATOL, POISON_INDEX, RTOL, Case, check_gather, check_scores, check_selection,
+from harness import (ATOL, POISON_BYTE, POISON_INDEX, RTOL, Case, check_gather, check_scores, check_selection,
                      check_unit, random_case)
 from kv_cache_compression_win_amd import chunkkv as ck
 
@@ -351,3 +351,36 @@ def test_select_any_scores_stays_in_range(T, c, w, l_max):
                 s = np.where(np.signbit(s), 0.0, s)            # sign bit -> 0
                 sel = oracle.topk(s, kk)
                 assert np.array_equal(idx, oracle.indices(T, w, c, sel))
+
+
+def test_gather_clamps_caller_indices_and_lengths():
+    # chunkkv_gather with caller-made indices and lengths: lengths are
+    # clamped into [0, L_cap] and index values into [0, T); rows past the
+    # clamped length keep their poison.
+    T, c, w, l_max, Hkv, d = 700, 10, 16, 200, 3, 128
+    prob = ck.make_problem(ck.BF16, [T], [l_max], 6, Hkv, d, w, c)
+    pl = ck.plan(prob)
+    L_cap = int(pl["l_cap"][0])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    k = torch.randn((T, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((T, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(5)
+    idx_h = rng.integers(-3 * T, 3 * T, size=pl["index_elems"]).astype(np.int32)
+    idx_h[:5] = [np.iinfo(np.int32).min, -1, T, T - 1, np.iinfo(np.int32).max]
+    len_h = np.array([L_cap + 50, -4, L_cap // 2], dtype=np.int32)
+    ko = torch.empty((pl["index_elems"], d), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    ko.view(torch.uint8).fill_(POISON_BYTE)
+    vo.view(torch.uint8).fill_(POISON_BYTE)
+    ck.gather(prob, k, v, torch.from_numpy(idx_h).cuda(), torch.from_numpy(len_h).cuda(), ko, vo)
+    torch.cuda.synchronize()
+    kh, vh = kvsynth.host_array(k), kvsynth.host_array(v)
+    ko_h, vo_h = kvsynth.host_array(ko), kvsynth.host_array(vo)
+    for h in range(Hkv):
+        n = min(max(int(len_h[h]), 0), L_cap)
+        rows = np.clip(idx_h[h * L_cap:h * L_cap + n].astype(np.int64), 0, T - 1)
+        for out, src in ((ko_h, kh), (vo_h, vh)):
+            blk = out[h * L_cap:(h + 1) * L_cap]
+            assert np.array_equal(blk[:n].view(np.uint16), src[rows, h].view(np.uint16))
+            assert np.all(blk[n:].view(np.uint8) == POISON_BYTE)
