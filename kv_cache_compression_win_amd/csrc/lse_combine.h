@@ -1,7 +1,6 @@
 // Device helpers of the log-sum-exp combine (ChunkKV page, section 4.1,
 // Algorithm 1 step 3, with every attention row normalised over all T keys as
-// in Kara eq. (1)).  Shared by the standalone combine kernel and the fused
-// combine + select kernel so that both give bit-identical chunk scores.
+// in Kara eq. (1)).
 //
 // Row r of a KV head has per-span statistics (m_s, l_s) with
 // l_s = sum over the span of 2^((x - m_s) * scale).  Then
@@ -23,30 +22,39 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2
   m = M;
 }
 
+// Threads that share one row in rows_lse: as many as fit with every row in
+// one pass (a power of two, 1 to 8).
+__host__ __device__ inline int lse_tpr(int R, int nthreads) {
+  int t = 8;
+  while (t > 1 && t * R > nthreads) t >>= 1;
+  return t;
+}
+
 // (M_r, L_r) of every row r < R from the n_span statistics (row stride 1,
-// span stride R_pad) into lse[r]: 8 consecutive threads share a row, thread
-// `sub` merging spans sub, sub + 8, ... in order (loads issued four at a
-// time), then a butterfly over the 8.  The arithmetic does not depend on
-// NTHREADS.
+// span stride R_pad) into lse[r]: tpr = lse_tpr(R, NTHREADS) consecutive
+// threads share a row, thread `sub` merging spans sub, sub + tpr, ... in
+// order (loads issued kUnr at a time, so a row of a few dozen spans costs one
+// or two memory round trips), then a butterfly over the tpr threads.  The
+// result depends only on R, NTHREADS and the statistics.
 template <int NTHREADS>
 __device__ __forceinline__ void rows_lse(const float2* st, int nspan, int R, int64_t R_pad, float scale,
                                          float2* lse) {
-  constexpr int kTPR = 8, kUnr = 4;
-  const int sub = threadIdx.x % kTPR;
-  for (int r = threadIdx.x / kTPR; r < R; r += NTHREADS / kTPR) {
+  constexpr int kUnr = 16;
+  const int tpr = lse_tpr(R, NTHREADS);
+  const int sub = threadIdx.x % tpr;
+  for (int r = threadIdx.x / tpr; r < R; r += NTHREADS / tpr) {
     float m = -INFINITY, l = 0.0f;
-    for (int s0 = sub; s0 < nspan; s0 += kTPR * kUnr) {
+    for (int s0 = sub; s0 < nspan; s0 += tpr * kUnr) {
       float2 ml[kUnr];
 #pragma unroll
       for (int u = 0; u < kUnr; ++u) {
-        const int s = s0 + u * kTPR;
+        const int s = s0 + u * tpr;
         ml[u] = s < nspan ? st[s * R_pad + r] : make_float2(-INFINITY, 0.0f);
       }
 #pragma unroll
       for (int u = 0; u < kUnr; ++u) lse_merge(m, l, ml[u].x, ml[u].y, scale);
     }
-#pragma unroll
-    for (int o = 1; o < kTPR; o <<= 1) {
+    for (int o = 1; o < tpr; o <<= 1) {
       const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
       lse_merge(m, l, m2, l2, scale);
     }
