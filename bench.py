@@ -27,25 +27,25 @@ if ROOT not in sys.path:
 
 METRIC = "KV tokens compressed/sec per layer·head-set + achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 
 
 SCORE_SOURCES = ("kv_cache_compression_win_amd/csrc/score_mfma.hip",
                  "kv_cache_compression_win_amd/csrc/chunkkv_internal.h")
 
 
-def counted_traffic(workload: str):
-    """HBM bytes per score-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or
-    None when there is none for this workload or the kernel source changed
-    since the counters were taken."""
+def profile_record(summary: str, workload: str, key: str):
+    """Value `key` of the machine-readable line in the committed rocprofv3
+    summary profiles/<summary>_<workload>.md, or None when there is none or
+    the score kernel's sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{summary}_{workload}.md")
     if not os.path.exists(path):
         return None
     rec = None
     with open(path) as f:
         for line in f:
-            if line.startswith("{") and "traffic_bytes_per_launch" in line:
+            if line.startswith("{") and key in line:
                 rec = json.loads(line)
     if rec is None:
         return None
@@ -53,7 +53,13 @@ def counted_traffic(workload: str):
     for rel in SCORE_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    return rec[key] if h.hexdigest() == rec["source_sha256"] else None
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per score-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain copy's readings)."""
+    return profile_record("hbm_counters", workload, "traffic_bytes_per_launch")
 
 
 def parse():
@@ -227,6 +233,9 @@ def main():
                         for kept in kept_per_anchor)
                   + accounting.gather_bytes(kept_total, wl.head_dim, e))
     score_gbps = score_kernel_bytes / (ph["score"] * 1e-3) / 1e9
+    # the score contraction: 2 * (G*w rows) * d per key token and KV head
+    score_flops = n_anchor * 2 * wl.window * wl.n_q_heads * wl.head_dim * sum(wl.seq_lens)
+    score_tflops = score_flops / (ph["score"] * 1e-3) / 1e12
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     layer_tokens = L * sum(wl.seq_lens)
     value = layer_tokens / (ms_step * 1e-3)
@@ -245,6 +254,9 @@ def main():
                      "traffic": counted_traffic(wl.name),
                      "algorithmic_bytes_per_launch": score_kernel_bytes,
                      "avg_launch_ms": ph["score"]},
+        "score_mfma": {"achieved": score_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": score_tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": score_flops,
+                       "busy_counted": profile_record("mfma_counters", wl.name, "mfma_busy_frac")},
         "step_hbm": {"achieved": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "algorithmic_bytes": step_bytes},
         "phases_ms": ph,
