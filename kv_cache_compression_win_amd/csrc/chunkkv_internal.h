@@ -26,12 +26,6 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #ifndef CKV_STAGE_TILES
 #define CKV_STAGE_TILES 4
 #endif
-// Cache policy of the score kernel's key loads (buffer instruction aux bits;
-// 2 = non-temporal: keys are read once, so they should not displace the chunk
-// partials and window queries in L2).
-#ifndef CKV_KAUX
-#define CKV_KAUX 2
-#endif
 #ifndef CKV_MIN_WAVES
 #define CKV_MIN_WAVES 2
 #endif
@@ -65,6 +59,9 @@ struct ScoreParams {
   int32_t wpu[kMaxSeqs];
   int32_t worker0[kMaxSeqs + 1];
   int32_t workers_per_layer;
+  // row blocks of one (head, span range) on workgroup ids 8 apart (one XCD),
+  // so the blocks' key reads meet in that XCD's L2
+  int32_t rb_interleave;
   int64_t tok0[kMaxSeqs];       // first K/V token row of sequence b
   int32_t qseq[kMaxSeqs];       // sequence index for q_stride_seq
   int32_t T[kMaxSeqs];

@@ -31,6 +31,13 @@ typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 constexpr int kD = 128;              // head_dim of this path
 // Buffer resource word 3 for raw dword loads on gfx9-family (CDNA) parts.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policies of the key loads (buffer instruction aux bits).  With one
+// row block per head every key is read once: non-temporal, so the keys do not
+// displace the chunk partials and window queries in L2.  With several row
+// blocks (G*w > 128) the blocks of a head read the same keys on one XCD at
+// about the same time: ordinary caching lets that XCD's L2 serve the repeats.
+constexpr int kKeysOnce = 2;
+constexpr int kKeysShared = 0;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
@@ -247,7 +254,7 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 // groups k+1 .. k+STAGES-1 -- of this item or the next ones -- are in flight.
 // The ring is indexed statically (the loop is unrolled by STAGES), so each
 // LDS store waits only for the loads of its own stage.
-template <int CC>
+template <int CC, int KAUX>
 __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
   __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
@@ -266,7 +273,15 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     int b = 0;
     while (b + 1 < P.n_seqs && wr >= tab.worker0[b + 1]) ++b;
     const int wpu = tab.wpu[b], ns = tab.n_span[b];
-    const int unit = (wr - tab.worker0[b]) / wpu, piece = (wr - tab.worker0[b]) % wpu;
+    const int m = wr - tab.worker0[b];
+    int unit = m / wpu, piece = m % wpu;
+    if (P.rb_interleave) {
+      // m = (g, rb, x) with x < 8: (head, piece) number g * 8 + x, row block rb
+      const int g = m / (8 * P.n_rb), x = m % 8, rb = (m / 8) % P.n_rb;
+      const int hp = g * 8 + x;
+      unit = (hp / wpu) * P.n_rb + rb;
+      piece = hp % wpu;
+    }
     const int base = li * P.items_per_layer + tab.item0[b] + unit * ns;
     lo = base + piece * ns / wpu;
     hi = base + (piece + 1) * ns / wpu;
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
         reinterpret_cast<void*>(it.kbase + static_cast<uint64_t>(gtok0) * st_bytes), 0,
         min(it.tok_end - gtok0, G::GROUP_TOK) * st_bytes, kBufferWord3);
 #pragma unroll
-    for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, CKV_KAUX);
+    for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
   };
   auto store_group = [&](const u32x4 (&src)[G::LOADS]) {
 #pragma unroll
@@ -471,7 +486,7 @@ int score_mfma_span_chunks(int chunk) {
 
 // Work split: about one workgroup per resident slot, each a balanced range of
 // consecutive spans of one unit.
-template <int CC>
+template <int CC, int KAUX>
 hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
   static thread_local int cached_dev = -1, cached_slots = 0;
   int dev = 0;
@@ -480,7 +495,7 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
   if (dev != cached_dev) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<CC>, kThreads, 0)) !=
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<CC, KAUX>, kThreads, 0)) !=
         hipSuccess)
       return e;
     cached_dev = dev;
@@ -495,14 +510,19 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
   }
   p.worker0[p.n_seqs] = w;
   p.workers_per_layer = w;
-  hipLaunchKernelGGL(score_mfma_kernel<CC>, dim3(w * p.n_layers), dim3(kThreads), 0, s, p);
+  // workgroups are dealt to the 8 XCDs in id order; the interleave needs every
+  // sequence's worker count to be a multiple of 8 * n_rb
+  p.rb_interleave = p.n_rb > 1 ? 1 : 0;
+  for (int b = 0; b < p.n_seqs; ++b)
+    if ((p.H_kv * p.wpu[b]) % 8 != 0) p.rb_interleave = 0;
+  hipLaunchKernelGGL((score_mfma_kernel<CC, KAUX>), dim3(w * p.n_layers), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <int CC>
 hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s) {
   if constexpr (pick_tiles(CC) >= 1)
-    return launch_split<CC>(p, n_items, s);
+    return p.n_rb > 1 ? launch_split<CC, kKeysShared>(p, n_items, s) : launch_split<CC, kKeysOnce>(p, n_items, s);
   else
     return hipErrorInvalidValue;
 }
