@@ -18,13 +18,15 @@
 // of selected chunks before j_w.
 //
 // Two kernels, one workgroup per (scoring layer, sequence, KV head):
-//   select_fast_kernel  256 threads, C <= 8192: scores in registers
-//     (chunk j in slot j / 256 of thread j % 256), counts by wave ballots,
+//   select_fast_kernel  512 threads, C <= 16384: scores in registers
+//     (chunk j in slot j / 512 of thread j % 512), counts by wave ballots,
 //     one barrier per greedy step, the selected ids compacted into LDS and
 //     the index list written position-parallel (coalesced).
 //   select_kernel       1024 threads, any C: scores in registers up to
 //     16384 chunks, else re-read from memory; one exclusive scan per tile
 //     of 1024 chunks places every kept token.
+#include <algorithm>
+
 #include "chunkkv_internal.h"
 
 namespace ckv {
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
 #endif
 constexpr int kFastThreads = CKV_SELECT_THREADS;
 constexpr int kFastWaves = kFastThreads / 64;
-constexpr int kFastMaxKPT = 128 / kFastWaves;   // (slot, wave) tables of at most 128 entries
+constexpr int kFastMaxKPT = 256 / kFastWaves;   // (slot, wave) tables of at most 256 entries
 constexpr int kFastMaxChunks = kFastThreads * kFastMaxKPT;
 constexpr int kFastTable = kFastMaxKPT * kFastWaves;
 
@@ -223,22 +225,29 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
 }
 
-// Exclusive prefix sum, in place, of tab[0 .. E) (E <= 128) by wave 0;
-// tab[E] receives the total.  Callers barrier before and after.
+// Exclusive prefix sum, in place, of tab[0 .. E) (E <= 256) by wave 0, four
+// consecutive entries per lane; tab[E] receives the total.  Callers barrier
+// before and after.
 __device__ __forceinline__ void wave0_scan_table(int* tab, int E) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  const int e0 = 2 * lane;
-  const int a = e0 < E ? tab[e0] : 0, b = e0 + 1 < E ? tab[e0 + 1] : 0;
-  int x = a + b;
+  const int e0 = 4 * lane;
+  int a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = e0 + i < E ? tab[e0 + i] : 0;
+  const int own = a[0] + a[1] + a[2] + a[3];
+  int x = own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  const int base = x - a - b;
-  if (e0 < E) tab[e0] = base;
-  if (e0 + 1 < E) tab[e0 + 1] = base + a;
+  int base = x - own;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e0 + i < E) tab[e0 + i] = base;
+    base += a[i];
+  }
   if (lane == 63) tab[E] = x;
 }
 
@@ -390,8 +399,11 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
 }
 
 template <int KPT>
-hipError_t launch_fast(const SelectParams& p, int n_blocks, int c_max, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(c_max) * sizeof(int);
+hipError_t launch_fast(const SelectParams& p, int n_blocks, hipStream_t s) {
+  // LDS for the selected chunk ids: exactly min(k, C) chunks are selected
+  int sel_max = 1;
+  for (int b = 0; b < p.n_seqs; ++b) sel_max = std::max(sel_max, std::min(p.kk[b], p.C[b]));
+  const size_t lds = static_cast<size_t>(sel_max) * sizeof(int);
   hipLaunchKernelGGL(select_fast_kernel<KPT>, dim3(n_blocks), dim3(kFastThreads), lds, s, p);
   return hipGetLastError();
 }
@@ -402,14 +414,14 @@ hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s) {
   int c_max = 1;
   for (int b = 0; b < p.n_seqs; ++b) c_max = p.C[b] > c_max ? p.C[b] : c_max;
   if (c_max <= kFastMaxChunks) {
-    if (c_max <= 1 * kFastThreads) return launch_fast<1>(p, n_blocks, c_max, s);
-    if (c_max <= 2 * kFastThreads) return launch_fast<2>(p, n_blocks, c_max, s);
-    if (c_max <= 4 * kFastThreads) return launch_fast<4>(p, n_blocks, c_max, s);
+    if (c_max <= 1 * kFastThreads) return launch_fast<1>(p, n_blocks, s);
+    if (c_max <= 2 * kFastThreads) return launch_fast<2>(p, n_blocks, s);
+    if (c_max <= 4 * kFastThreads) return launch_fast<4>(p, n_blocks, s);
     if constexpr (kFastMaxKPT >= 8)
-      if (c_max <= 8 * kFastThreads) return launch_fast<8>(p, n_blocks, c_max, s);
+      if (c_max <= 8 * kFastThreads) return launch_fast<8>(p, n_blocks, s);
     if constexpr (kFastMaxKPT >= 16)
-      if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, c_max, s);
-    if constexpr (kFastMaxKPT >= 32) return launch_fast<32>(p, n_blocks, c_max, s);
+      if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, s);
+    if constexpr (kFastMaxKPT >= 32) return launch_fast<32>(p, n_blocks, s);
   }
   hipLaunchKernelGGL(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
   return hipGetLastError();
