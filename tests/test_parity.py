@@ -77,11 +77,18 @@ def test_generic_path(dtype, d, c, Hq, Hkv, w):
     _all_units(case)
 
 
-@pytest.mark.parametrize("Hq,Hkv,w", [(3, 1, 5), (24, 8, 7), (64, 8, 64), (8, 8, 32), (32, 4, 48)])
-def test_mfma_row_blocks(Hq, Hkv, w):
+@pytest.mark.parametrize("Hq,Hkv,w,c", [
+    (3, 1, 5, 10), (24, 8, 7, 10), (8, 8, 32, 10),    # one row block, padding rows
+    (64, 8, 64, 10), (64, 8, 64, 32),                 # 4 row blocks (the 70B shape)
+    (64, 8, 64, 5), (64, 8, 64, 20),                  # 4 row blocks, 1 and 4 tiles per group
+    (16, 2, 32, 10), (16, 2, 32, 5),                  # 2 row blocks, 2 KV heads
+    (32, 4, 48, 10),                                  # 3 row blocks
+])
+def test_mfma_row_blocks(Hq, Hkv, w, c):
     # G*w not a multiple of 32 (padding rows), and G*w > 128 (several row
-    # blocks per head: 64/8 heads x w=64 is the 70B shape).
-    case = random_case(ck.BF16, [1500], [160], Hq, Hkv, 128, w, 10, seed=Hq * w).run()
+    # blocks per head, each its own workgroup; blocks of one span range are
+    # placed on one XCD when the worker counts allow).
+    case = random_case(ck.BF16, [1500], [160], Hq, Hkv, 128, w, c, seed=Hq * w + c).run()
     _all_units(case)
 
 
