@@ -38,6 +38,7 @@ constexpr int kBufferWord3 = 0x00020000;
 // about the same time: ordinary caching lets that XCD's L2 serve the repeats.
 constexpr int kKeysOnce = 2;
 constexpr int kKeysShared = 0;
+constexpr int kSharedKeySpans = 8;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
@@ -501,7 +502,12 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
     cached_dev = dev;
     cached_slots = cus * (per_cu > 0 ? per_cu : 1);
   }
-  const int per_worker = (n_items + cached_slots - 1) / cached_slots;  // spans per workgroup, target
+  // spans per workgroup: about one workgroup per resident slot; with several
+  // row blocks per head at most kSharedKeySpans, so that the blocks of a span
+  // range (dispatched together onto one XCD) stay close enough in time for
+  // that XCD's L2 to serve their repeated key reads
+  int per_worker = (n_items + cached_slots - 1) / cached_slots;
+  if (p.n_rb > 1 && per_worker > kSharedKeySpans) per_worker = kSharedKeySpans;
   int w = 0;
   for (int b = 0; b < p.n_seqs; ++b) {
     p.wpu[b] = (p.n_span[b] + per_worker - 1) / per_worker;
