@@ -9,8 +9,9 @@ the timed region.
 
 Prints one JSON line: layer-tokens/s (sum over layers of the tokens
 compressed, per second), the score kernel's achieved HBM bandwidth against
-the 8 TB/s MI355X peak (phase events recorded by the library on the launch
-stream), and the CPU oracle timed on a bounded sample of the same workload.
+the 8 TB/s MI355X peak (the library's phase events, taken at the score
+kernel's own start and end on the launch stream), and the CPU oracle timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 

@@ -192,12 +192,18 @@ int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
  *   workspace       DEVICE scratch of >= chunkkv_workspace_bytes(p, 1) bytes;
  *                   a larger one lets more anchor layers share a launch
  *   phase_events    NULL, or HOST [CHUNKKV_N_PHASE_EVENTS] hipEvent_t handles
- *                   recorded on `stream` before the score kernels, after
- *                   them, after the combine + selection kernels and after
- *                   the gathers (for timing; any entry may be NULL).  When
- *                   the workspace cannot hold every scoring layer at once,
- *                   the phases interleave and entry 1 is recorded together
- *                   with entry 2.
+ *                   marking, on `stream`, the start of the scoring phase,
+ *                   its end, the start of the gather phase and its end (for
+ *                   timing; any entry may be NULL).  A phase that is a
+ *                   single kernel launch (the bf16 d=128 score kernel over
+ *                   every scoring layer; the gather over at most 32 layers;
+ *                   at most 32 sequences) takes its two events at that
+ *                   kernel's start and end (hipExtLaunchKernel), so no
+ *                   marker separates the kernels of a call; otherwise they
+ *                   are recorded between the phases' kernels.  When the
+ *                   workspace cannot hold every scoring layer at once, the
+ *                   phases interleave and entry 1 is recorded together with
+ *                   entry 2.
  * Errors: INVALID_ARG (incl. n_layers < 1, n_reuse < 1, a NULL table entry
  * that is needed), UNSUPPORTED, WORKSPACE, HIP.
  */

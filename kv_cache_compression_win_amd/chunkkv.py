@@ -102,9 +102,9 @@ def hip_runtime() -> ctypes.CDLL:
 
 class PhaseEvents:
     """CHUNKKV_N_PHASE_EVENTS raw hipEvent_t handles for chunkkv_compress_layers'
-    phase_events argument: recorded on the launch stream before the score
-    kernels, after them, after the combine + selection kernels and after the
-    gathers."""
+    phase_events argument: start and end of the scoring phase, start and end
+    of the gather phase, on the launch stream (taken at the kernel's own start
+    and end where a phase is one launch)."""
 
     def __init__(self):
         H = hip_runtime()

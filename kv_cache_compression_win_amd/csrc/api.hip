@@ -160,8 +160,10 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
 
 // ------------------------------------------------------------- launchers --
 
+// ev_start / ev_stop (null, or only with one sequence batch and the MFMA
+// kernel) are recorded at the score kernel's start and end.
 hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U,
-                     float2* st, hipStream_t s) {
+                     float2* st, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
     ScoreParams P{};
@@ -208,7 +210,8 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
     P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
     P.rebase_raw = kRebaseLog2 / P.scale;
     const int nblk = nl * items;
-    const hipError_t e = pl.mfma ? launch_score_mfma(P, nblk, s) : launch_score_generic(P, pl.dtype, nblk, s);
+    const hipError_t e = pl.mfma ? launch_score_mfma(P, nblk, s, ev_start, ev_stop)
+                                 : launch_score_generic(P, pl.dtype, nblk, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -296,7 +299,8 @@ hipError_t run_select(const Plan& pl, int nl, const float* scores, int32_t* indi
 // Gathers layers [l0, l0 + nl); layer l reads index block blocks[l - l0].
 hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* const* v,
                       void* const* ko, void* const* vo, const int32_t* blocks, const int32_t* indices,
-                      const int32_t* lengths, hipStream_t s) {
+                      const int32_t* lengths, hipStream_t s, hipEvent_t ev_start = nullptr,
+                      hipEvent_t ev_stop = nullptr) {
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
     GatherParams P{};
@@ -331,7 +335,7 @@ hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* 
     P.row_bytes = pl.d * pl.eb;
     P.kv_st_bytes = pl.kv_st * pl.eb;
     P.kv_sh_bytes = pl.kv_sh * pl.eb;
-    const hipError_t e = launch_gather(P, nl * items, s);
+    const hipError_t e = launch_gather(P, nl * items, s, ev_start, ev_stop);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -460,18 +464,19 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
   while (batch > 1 && pl.ws_bytes(batch) > workspace_bytes) --batch;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto record = [&](int i) -> hipError_t {
-    if (phase_events && phase_events[i])
-      return hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s);
-    return hipSuccess;
-  };
-  hipError_t e = record(0);
+  auto ev = [&](int i) { return phase_events ? static_cast<hipEvent_t>(phase_events[i]) : nullptr; };
+  auto record = [&](int i) -> hipError_t { return ev(i) ? hipEventRecord(ev(i), s) : hipSuccess; };
+  const bool one_batch = n_anchor <= batch;
+  // a phase that is one kernel launch takes its events at that kernel's start
+  // and end (no separate stream markers between the kernels of a step)
+  const bool score_events = one_batch && pl.mfma && pl.B <= kMaxSeqs;
+  const bool gather_events = n_layers <= kMaxLayers && pl.B <= kMaxSeqs;
+  hipError_t e = score_events ? hipSuccess : record(0);
   if (e != hipSuccess) return hip_fail(e, "phase event");
 
   float* U;
   float2 *st, *lse;
   carve(pl, batch, workspace, &U, &st, &lse);
-  const bool one_batch = n_anchor <= batch;
   const void* qb[kMaxLayers];
   const void* kb[kMaxLayers];
   for (int a0 = 0; a0 < n_anchor; a0 += batch) {
@@ -480,8 +485,10 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
       qb[i] = q_win[(a0 + i) * n_reuse];
       kb[i] = k[(a0 + i) * n_reuse];
     }
-    if ((e = run_score(pl, na, qb, kb, U, st, s)) != hipSuccess) return hip_fail(e, "score launch");
-    if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
+    if ((e = score_events ? run_score(pl, na, qb, kb, U, st, s, ev(0), ev(1)) : run_score(pl, na, qb, kb, U, st, s)) !=
+        hipSuccess)
+      return hip_fail(e, "score launch");
+    if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
     if ((e = run_combine(pl, na, U, st, lse, scores + a0 * pl.scores_elems, s)) != hipSuccess)
       return hip_fail(e, "combine launch");
     if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
@@ -489,17 +496,18 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
       return hip_fail(e, "select launch");
   }
   if (!one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-  if ((e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
+  if (!gather_events && (e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
 
   int32_t blocks[kMaxLayers];
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, n_layers - l0);
     for (int i = 0; i < nl; ++i) blocks[i] = (l0 + i) / n_reuse;
-    if ((e = run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s)) !=
-        hipSuccess)
-      return hip_fail(e, "gather launch");
+    e = gather_events ? run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s,
+                                   ev(2), ev(3))
+                      : run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
-  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+  if (!gather_events && (e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
   return ok();
 }
 

@@ -2,6 +2,7 @@
 // libchunkkv.so (gfx950 / CDNA4).  Not part of the C-ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -164,7 +165,9 @@ struct GatherParams {
 bool score_mfma_supported(int chunk);
 int score_mfma_span_chunks(int chunk);
 // Launches min(n_items, resident workgroups) persistent workgroups.
-hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s);
+// ev_start / ev_stop (may be null) are recorded at the kernel's start and end.
+hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 // Generic path: any dtype / head_dim / chunk size (VALU fp32).
 int score_generic_span_chunks(int R_pad, int chunk);
 size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d);
@@ -173,6 +176,7 @@ int combine_spans_per_blk(int R_pad);
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_row_lse(const CombineParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s);
-hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 
 }  // namespace ckv

@@ -83,9 +83,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) 
 
 }  // namespace
 
-hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(gather_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
+  GatherParams arg = p;
+  void* args[] = {&arg};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&gather_kernel), dim3(n_blocks), dim3(kThreads), args, 0,
+                            s, ev_start, ev_stop, 0);
 }
 
 }  // namespace ckv

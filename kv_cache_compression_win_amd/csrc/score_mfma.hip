@@ -488,7 +488,7 @@ int score_mfma_span_chunks(int chunk) {
 // Work split: about one workgroup per resident slot, each a balanced range of
 // consecutive spans of one unit.
 template <int CC, int KAUX>
-hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
+hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   static thread_local int cached_dev = -1, cached_slots = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -521,23 +521,25 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s) {
   p.rb_interleave = p.n_rb > 1 ? 1 : 0;
   for (int b = 0; b < p.n_seqs; ++b)
     if ((p.H_kv * p.wpu[b]) % 8 != 0) p.rb_interleave = 0;
-  hipLaunchKernelGGL((score_mfma_kernel<CC, KAUX>), dim3(w * p.n_layers), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  void* args[] = {&p};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&score_mfma_kernel<CC, KAUX>), dim3(w * p.n_layers),
+                            dim3(kThreads), args, 0, s, ev_start, ev_stop, 0);
 }
 
 template <int CC>
-hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s) {
+hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if constexpr (pick_tiles(CC) >= 1)
-    return p.n_rb > 1 ? launch_split<CC, kKeysShared>(p, n_items, s) : launch_split<CC, kKeysOnce>(p, n_items, s);
+    return p.n_rb > 1 ? launch_split<CC, kKeysShared>(p, n_items, s, e0, e1)
+                      : launch_split<CC, kKeysOnce>(p, n_items, s, e0, e1);
   else
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s) {
+hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   switch (p.c) {
 #define CKV_CASE(c) \
   case c:           \
-    return launch_if_laid_out<c>(p, n_items, s);
+    return launch_if_laid_out<c>(p, n_items, s, ev_start, ev_stop);
     CKV_CHUNKS(CKV_CASE)
 #undef CKV_CASE
     default:
