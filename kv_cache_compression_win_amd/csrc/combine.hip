@@ -25,10 +25,8 @@ constexpr int kWeightFloats = 16384;  // weights of one item's spans (64 KB at m
 
 template <int QPT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
-  // dynamic LDS: lse [R_pad] float2, then weights [spans_per_blk][R_pad]
-  extern __shared__ float smem[];
-  float2* lse = reinterpret_cast<float2*>(smem);
-  float* wts = smem + 2 * P.R_pad;
+  // dynamic LDS: weights [spans_per_blk][R_pad]
+  extern __shared__ float wts[];
   const int tid = threadIdx.x;
 
   const int li = blockIdx.x / P.items_per_layer;
@@ -44,13 +42,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
   const float2* st = P.stats + li * P.st_layer_stride + P.st_off[b] +
                      static_cast<int64_t>(h) * nspan * P.R_pad;
   const float2* lse_g = P.lse + li * P.lse_layer_stride + P.lse_off[b] + static_cast<int64_t>(h) * P.R_pad;
-  for (int r = tid; r < P.R; r += kThreads) lse[r] = lse_g[r];
-  __syncthreads();
   const int s_lo = blk * P.spans_per_blk;
   const int ns = min(P.spans_per_blk, nspan - s_lo);
+  // the row statistics and the spans' maxima are read together (one memory
+  // round trip before the weights)
   for (int e = tid; e < ns * P.R_pad; e += kThreads) {
     const int s = e / P.R_pad, r = e - s * P.R_pad;
-    wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse[r], P.scale)
+    wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse_g[r], P.scale)
                      : 0.0f;
   }
   __syncthreads();
@@ -92,8 +90,7 @@ int combine_spans_per_blk(int R_pad) {
 
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
   if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
-  const size_t lds = (static_cast<size_t>(2) * p.R_pad + static_cast<size_t>(p.spans_per_blk) * p.R_pad) *
-                     sizeof(float);
+  const size_t lds = static_cast<size_t>(p.spans_per_blk) * p.R_pad * sizeof(float);
   switch (combine_qpt(p.R_pad)) {
     case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
     case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
