@@ -165,6 +165,15 @@ struct GatherParams {
 bool score_mfma_supported(int chunk);
 int score_mfma_span_chunks(int chunk);
 // Launches min(n_items, resident workgroups) persistent workgroups.
+// Launches `kernel` with one by-value argument and returns the launch's own
+// status (not a sticky error left by an earlier, unrelated HIP call).
+template <typename Arg>
+inline hipError_t launch1(void (*kernel)(Arg), dim3 grid, dim3 block, size_t lds, hipStream_t s, Arg arg,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+  void* args[] = {&arg};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s, ev_start, ev_stop, 0);
+}
+
 // ev_start / ev_stop (may be null) are recorded at the kernel's start and end.
 hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start = nullptr,
                              hipEvent_t ev_stop = nullptr);

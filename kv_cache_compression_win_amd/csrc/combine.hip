@@ -79,8 +79,7 @@ __global__ __launch_bounds__(kThreads) void row_lse_kernel(const CombineParams P
 }  // namespace
 
 hipError_t launch_row_lse(const CombineParams& p, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(row_lse_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch1(row_lse_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p);
 }
 
 int combine_spans_per_blk(int R_pad) {
@@ -92,14 +91,13 @@ hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
   if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(p.spans_per_blk) * p.R_pad * sizeof(float);
   switch (combine_qpt(p.R_pad)) {
-    case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
-    case 8: hipLaunchKernelGGL(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
-    case 16: hipLaunchKernelGGL(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), lds, s, p); break;
+    case 1: return launch1(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+    case 2: return launch1(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+    case 4: return launch1(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+    case 8: return launch1(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+    case 16: return launch1(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), lds, s, p);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace ckv

@@ -85,10 +85,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams P) 
 
 hipError_t launch_gather(const GatherParams& p, int n_blocks, hipStream_t s, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {
-  GatherParams arg = p;
-  void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&gather_kernel), dim3(n_blocks), dim3(kThreads), args, 0,
-                            s, ev_start, ev_stop, 0);
+  return launch1(gather_kernel, dim3(n_blocks), dim3(kThreads), 0, s, p, ev_start, ev_stop);
 }
 
 }  // namespace ckv

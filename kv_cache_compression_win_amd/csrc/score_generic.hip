@@ -133,11 +133,8 @@ size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d) {
 
 hipError_t launch_score_generic(const ScoreParams& p, int dtype, int n_blocks, hipStream_t s) {
   const size_t lds = score_generic_lds_bytes(p.R_pad, p.span_chunks, p.d);
-  if (dtype == 0)
-    hipLaunchKernelGGL(score_generic_kernel<float>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-  else
-    hipLaunchKernelGGL(score_generic_kernel<__bf16>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-  return hipGetLastError();
+  if (dtype == 0) return launch1(score_generic_kernel<float>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+  return launch1(score_generic_kernel<__bf16>, dim3(n_blocks), dim3(kThreads), lds, s, p);
 }
 
 }  // namespace ckv

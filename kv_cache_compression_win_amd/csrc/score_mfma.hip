@@ -521,9 +521,7 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev
   p.rb_interleave = p.n_rb > 1 ? 1 : 0;
   for (int b = 0; b < p.n_seqs; ++b)
     if ((p.H_kv * p.wpu[b]) % 8 != 0) p.rb_interleave = 0;
-  void* args[] = {&p};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&score_mfma_kernel<CC, KAUX>), dim3(w * p.n_layers),
-                            dim3(kThreads), args, 0, s, ev_start, ev_stop, 0);
+  return launch1(score_mfma_kernel<CC, KAUX>, dim3(w * p.n_layers), dim3(kThreads), 0, s, p, ev_start, ev_stop);
 }
 
 template <int CC>

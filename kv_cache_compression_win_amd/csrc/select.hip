@@ -404,8 +404,7 @@ hipError_t launch_fast(const SelectParams& p, int n_blocks, hipStream_t s) {
   int sel_max = 1;
   for (int b = 0; b < p.n_seqs; ++b) sel_max = std::max(sel_max, std::min(p.kk[b], p.C[b]));
   const size_t lds = static_cast<size_t>(sel_max) * sizeof(int);
-  hipLaunchKernelGGL(select_fast_kernel<KPT>, dim3(n_blocks), dim3(kFastThreads), lds, s, p);
-  return hipGetLastError();
+  return launch1(select_fast_kernel<KPT>, dim3(n_blocks), dim3(kFastThreads), lds, s, p);
 }
 
 }  // namespace
@@ -423,8 +422,7 @@ hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s) {
       if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, s);
     if constexpr (kFastMaxKPT >= 32) return launch_fast<32>(p, n_blocks, s);
   }
-  hipLaunchKernelGGL(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
-  return hipGetLastError();
+  return launch1(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
 }
 
 }  // namespace ckv
