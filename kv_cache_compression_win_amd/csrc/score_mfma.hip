@@ -3,10 +3,12 @@
 // softmax(QK^T / sqrt(d)) of Kara eq. (1).
 //
 // Work item = (layer, sequence, KV head, 128-row block of the G*w window
-// rows, span of whole chunks).  Persistent workgroups walk contiguous ranges
-// of items; keys are streamed HBM -> VGPR -> LDS once, one group ahead.
-// Logits come from v_mfma_f32_32x32x16_bf16 with the KEYS as the A operand (32 token slots x 16 dims) and the window queries as B (16 dims x
-// 32 query rows), so in the 32x32 fp32 result each lane owns one query row
+// rows, span of whole chunks).  Workgroups (about one per resident slot; more,
+// with shorter ranges, when a head has several row blocks) walk contiguous
+// ranges of items; keys are streamed HBM -> VGPR -> LDS once, a register ring
+// of groups ahead.  Logits come from v_mfma_f32_32x32x16_bf16 with the KEYS as
+// the A operand (32 token slots x 16 dims) and the window queries as B (16
+// dims x 32 query rows), so in the 32x32 fp32 result each lane owns one query row
 // and 16 token slots.  Token slots are permuted so that each lane half holds
 // CPH whole chunks: the chunk sums are then straight-line adds fixed at
 // compile time for each chunk size.  The logits never leave registers: the
@@ -485,8 +487,8 @@ int score_mfma_span_chunks(int chunk) {
   }
 }
 
-// Work split: about one workgroup per resident slot, each a balanced range of
-// consecutive spans of one unit.
+// Work split: balanced ranges of consecutive spans of one unit, about one
+// workgroup per resident slot (shorter ranges for heads of several row blocks).
 template <int CC, int KAUX>
 hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   static thread_local int cached_dev = -1, cached_slots = 0;
