@@ -162,6 +162,16 @@ def test_layer_index_reuse(n_reuse):
     assert case.scores.shape[0] == -(-5 // n_reuse)
 
 
+@pytest.mark.parametrize("n_reuse", [1, 2])
+def test_more_layers_than_one_launch(n_reuse):
+    # more than 32 layers in one call: the scoring layers are split over
+    # several launches (32 at most each) and so are the gathers.
+    case = random_case(ck.BF16, [300, 517], [40, 60], 8, 2, 128, 16, 10, n_layers=35,
+                       n_reuse=n_reuse, seed=35 + n_reuse).run()
+    _all_units(case)
+    assert case.scores.shape[0] == -(-35 // n_reuse)
+
+
 def test_strided_kv_layout():
     # K/V with a padded head stride (d + 64 elements) and token stride.
     Hkv, d, T = 2, 128, 1100
