@@ -217,9 +217,21 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
   return hipSuccess;
 }
 
+// Combine blocks a launch should have (2 per CU of a 256-CU part) before
+// spans per block are reduced.
+constexpr int64_t kCombineMinBlocks = 512;
+
 hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
                        hipStream_t s) {
-  const int spb = combine_spans_per_blk(pl.R_pad);
+  // spans per combine block: fewer when the launch would otherwise have too
+  // few blocks to spread over the GPU (a layer or two of short sequences)
+  int spb = combine_spans_per_blk(pl.R_pad);
+  auto n_blocks = [&](int per) {
+    int64_t n = 0;
+    for (const Seq& sq : pl.seq) n += static_cast<int64_t>(pl.Hkv) * ((sq.n_span + per - 1) / per);
+    return n * nl;
+  };
+  while (spb > 1 && n_blocks(spb) < kCombineMinBlocks) spb /= 2;
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
     CombineParams P{};
