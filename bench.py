@@ -66,8 +66,8 @@ def counted_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="llama3-8b-32layer-T32768")
     ap.add_argument("--layers", type=int, default=None, help="use the first N layers only")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
