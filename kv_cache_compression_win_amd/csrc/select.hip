@@ -6,9 +6,10 @@
 // patterns is the value order.  tau = the largest 32-bit pattern v with
 // #{S_j >= v} >= k is built greedily from the top bit (bit 30 alone, then two
 // bits per workgroup-wide count of three candidates); it is exactly the k-th
-// largest score.  A chunk is selected if its score is above tau, or equal to
-// tau and among the first k - #{S > tau} equal ones in id order (lower chunk
-// id first).
+// largest score.  The search stops as soon as exactly k chunks reach the
+// prefix built so far: they are the selection whatever the lower bits.  A
+// chunk is selected if its score is above tau, or equal to tau and among the
+// first k - #{S > tau} equal ones in id order (lower chunk id first).
 //
 // Index list: with j_w = floor((T - w) / c), the first chunk that reaches the
 // recent window [T - w, T), the kept tokens in ascending order are the c
@@ -142,8 +143,18 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
       return cnt;
     };
     unsigned prefix = 0;
-    if (block_sum(count_ge(1u << 30), red) >= kk) prefix = 1u << 30;
-    for (int bit = 28; bit >= 0; bit -= 2) {
+    int n_pre = C;   // #{S_j >= prefix}
+    {
+      const int t = block_sum(count_ge(1u << 30), red);
+      if (t >= kk) {
+        prefix = 1u << 30;
+        n_pre = t;
+      }
+    }
+    // once exactly k chunks reach the prefix they are the selection: the
+    // remaining bits cannot change it (the k-th largest is >= prefix, the
+    // (k+1)-th below it), so the search stops there
+    for (int bit = 28; bit >= 0 && n_pre != kk; bit -= 2) {
       const unsigned c1 = prefix | (1u << bit), c2 = prefix | (2u << bit), c3 = prefix | (3u << bit);
       int3 cnt = make_int3(0, 0, 0);
       if (in_regs) {
@@ -162,7 +173,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const SelectPara
         }
       }
       const int3 tot = block_sum3(cnt, red3);
-      prefix = tot.z >= kk ? c3 : tot.y >= kk ? c2 : tot.x >= kk ? c1 : prefix;
+      if (tot.z >= kk) {
+        prefix = c3;
+        n_pre = tot.z;
+      } else if (tot.y >= kk) {
+        prefix = c2;
+        n_pre = tot.y;
+      } else if (tot.x >= kk) {
+        prefix = c1;
+        n_pre = tot.x;
+      }
     }
     tau = prefix;
     int gt = 0;
@@ -308,7 +328,8 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
         n_ge = t.x;
       }
     }
-    for (int bit = 28; bit >= 0; bit -= 2) {
+    // stops once exactly k chunks reach tau (see select_kernel)
+    for (int bit = 28; bit >= 0 && n_ge != kk; bit -= 2) {
       const unsigned c1 = tau | (1u << bit), c2 = tau | (2u << bit), c3 = tau | (3u << bit);
       int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
