@@ -204,6 +204,9 @@ int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
  *                   workspace cannot hold every scoring layer at once, the
  *                   phases interleave and entry 1 is recorded together with
  *                   entry 2.
+ * The call allocates nothing and issues no memset or copy, only kernel
+ * launches (and the phase events): without phase events it can be captured
+ * into a HIP graph, whose replays give the same outputs.
  * Errors: INVALID_ARG (incl. n_layers < 1, n_reuse < 1, a NULL table entry
  * that is needed), UNSUPPORTED, WORKSPACE, HIP.
  */

@@ -172,6 +172,43 @@ def test_more_layers_than_one_launch(n_reuse):
     assert case.scores.shape[0] == -(-35 // n_reuse)
 
 
+def test_graph_capture_replays_match_eager():
+    # chunkkv_compress_layers allocates nothing and records no memsets, so a
+    # call can be captured in a HIP graph; every replay (with eager work and
+    # synchronisations between them) must reproduce the eager outputs bit for
+    # bit.
+    case = random_case(ck.BF16, [4096, 1500], [400, 150], 32, 8, 128, 32, 10, n_layers=4, n_reuse=2,
+                       seed=7).run()
+    ref = case.bufs
+    L = case.L
+    bufs = ck.Buffers(case.prob, L, case.n_reuse, case.d, torch.bfloat16, "cuda")
+    qs = [case.q_win[l] if l % case.n_reuse == 0 else None for l in range(L)]
+    stream = torch.cuda.Stream()
+    args = (case.prob, case.n_reuse, qs, [case.k[l] for l in range(L)], [case.v[l] for l in range(L)],
+            [bufs.k_out[l] for l in range(L)], [bufs.v_out[l] for l in range(L)], bufs.scores, bufs.indices,
+            bufs.lengths, bufs.workspace, bufs.ws_bytes)
+    with torch.cuda.stream(stream):
+        ck.compress_layers(*args, stream=stream)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        ck.compress_layers(*args, stream=stream)
+    torch.cuda.synchronize()
+    outs = (bufs.scores, bufs.indices, bufs.lengths, bufs.k_out, bufs.v_out)
+    refs = (ref.scores, ref.indices, ref.lengths, ref.k_out, ref.v_out)
+    for rep in range(3):
+        # eager work between replays: the same poison as the eager run (rows
+        # past each head's length are left untouched by the library)
+        for t in (bufs.scores, bufs.lengths, bufs.k_out, bufs.v_out):
+            t.view(torch.uint8).fill_(POISON_BYTE)
+        bufs.indices.fill_(POISON_INDEX)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, refs):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
+
+
 def test_strided_kv_layout():
     # K/V with a padded head stride (d + 64 elements) and token stride.
     Hkv, d, T = 2, 128, 1100
