@@ -197,10 +197,10 @@ int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
  *                   timing; any entry may be NULL).  A phase that is a
  *                   single kernel launch (the bf16 d=128 score kernel over
  *                   every scoring layer; the gather over at most 32 layers;
- *                   at most 32 sequences) takes its two events at that
- *                   kernel's start and end (hipExtLaunchKernel), so no
- *                   marker separates the kernels of a call; otherwise they
- *                   are recorded between the phases' kernels.  When the
+ *                   at most 8 sequences) takes its two events at that
+ *                   kernel's own start and end (hipExtLaunchKernel);
+ *                   otherwise they are recorded between the phases'
+ *                   kernels.  When the
  *                   workspace cannot hold every scoring layer at once, the
  *                   phases interleave and entry 1 is recorded together with
  *                   entry 2.
