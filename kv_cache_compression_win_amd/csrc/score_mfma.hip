@@ -42,6 +42,7 @@ constexpr int kKeysOnce = 2;
 constexpr int kKeysShared = 0;
 constexpr int kSharedKeySpans = 8;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
+constexpr int kLdsAhead = 4;         // key fragment reads issued ahead of their MFMA
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
 // Number of 32-slot MFMA tiles per group for chunk size c (slots per lane
@@ -260,6 +261,8 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 template <int CC, int KAUX>
 __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
+  constexpr int kLoadEvery = G::NT * kKSteps / G::LOADS;   // MFMAs per key load of the next group
+  static_assert(kLoadEvery * G::LOADS == G::NT * kKSteps, "key loads must spread evenly over the MFMAs");
   __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
   __shared__ float u_lds[G::SPAN_CHUNKS * kMfmaRows];
   __shared__ Tables tab;
@@ -326,13 +329,10 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     const int lam = min(16 * tau + 4 * (i >> 3) + (i & 3), G::HALF_TOK - 1);
     voff[x] = (((i >> 2) & 1) * G::HALF_TOK + lam) * st_bytes + p * 16;
   }
-  auto load_group = [&](u32x4 (&dst)[G::LOADS], const Item& it, int gi) {
+  auto group_rsrc = [&](const Item& it, int gi) {
     const int gtok0 = it.tok_begin + gi * G::GROUP_TOK;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(it.kbase + static_cast<uint64_t>(gtok0) * st_bytes), 0,
-        min(it.tok_end - gtok0, G::GROUP_TOK) * st_bytes, kBufferWord3);
-#pragma unroll
-    for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(it.kbase + static_cast<uint64_t>(gtok0) * st_bytes),
+                                             0, min(it.tok_end - gtok0, G::GROUP_TOK) * st_bytes, kBufferWord3);
   };
   auto store_group = [&](const u32x4 (&src)[G::LOADS]) {
 #pragma unroll
@@ -385,10 +385,16 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   // the last group is loaded again (its data is never used), so the number of
   // loads younger than any stage is fixed and each stage store waits only
   // for its own loads.
-  auto load_next = [&](u32x4 (&dst)[G::LOADS]) {
-    load_group(dst, lc.it, lc.g);
+  auto next_rsrc = [&]() {
+    const __amdgpu_buffer_rsrc_t rsrc = group_rsrc(lc.it, lc.g);
     Cursor t = lc;
     if (cursor_next<CC>(P, tab, t, hi)) lc = t;
+    return rsrc;
+  };
+  auto load_next = [&](u32x4 (&dst)[G::LOADS]) {
+    const __amdgpu_buffer_rsrc_t rsrc = next_rsrc();
+#pragma unroll
+    for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
   };
   load_q(cc.it);
   // issue the stages strictly in ring order (stage 0 oldest)
@@ -411,7 +417,10 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     __syncthreads();  // previous group's LDS reads (and any flush) are done
     store_group(regs[S]);
     __syncthreads();
-    load_next(regs[S]);
+    // the next group's loads go out one per kLoadEvery MFMAs of this group
+    // (issued together right after the barrier, the 4 waves' loads queue up
+    // at the vector-memory unit); past the end of the range, all at once
+    const __amdgpu_buffer_rsrc_t rsrc = next_rsrc();
     if (live) {
       f32x16 acc[G::NT];
 #pragma unroll
@@ -419,10 +428,22 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
         acc[tau] = f32x16{};
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
+          const int mi = tau * kKSteps + s;
+          if (mi % kLoadEvery == 0)
+            regs[S][mi / kLoadEvery] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[mi / kLoadEvery], 0, KAUX);
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
               &k_lds[(tau * 32 + n) * kPieces + ((8 * ho + s) ^ (n & 15))]);
           acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc[tau], 0, 0, 0);
         }
+      }
+      // schedule: the first kLdsAhead fragment reads, then per MFMA: its
+      // key load (every kLoadEvery-th), the MFMA, the fragment read kLdsAhead ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+#pragma unroll
+      for (int mi = 0; mi < G::NT * kKSteps; ++mi) {
+        if (mi % kLoadEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (mi + kLdsAhead < G::NT * kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       const Item& it = cc.it;
       const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
@@ -435,6 +456,9 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
         l_acc = 0.0f;
       }
       cursor_next<CC>(P, tab, cc, hi);
+    } else {
+#pragma unroll
+      for (int x = 0; x < G::LOADS; ++x) regs[S][x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
     }
   };
   const int rounds = (total + G::STAGES - 1) / G::STAGES;
