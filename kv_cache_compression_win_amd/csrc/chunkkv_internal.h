@@ -101,6 +101,7 @@ struct CombineParams {
   int64_t score_off[kMaxSeqs];
   int64_t lse_off[kMaxSeqs];    // per-row (M, L) of sequence b: [H_kv][R_pad] float2
   int32_t head0[kMaxSeqs + 1];  // first (sequence, head) item of sequence b in the row-statistics launch
+  int32_t fuse_lse;             // 1: each combine block forms its head's (M_r, L_r) itself (no row-statistics launch)
   int64_t u_layer_stride, st_layer_stride, score_layer_stride, lse_layer_stride;
   const float* U;
   const float2* stats;

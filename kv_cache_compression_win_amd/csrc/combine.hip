@@ -10,7 +10,10 @@
 // KV head) from the span statistics; combine_kernel's work item is (layer,
 // sequence, KV head, block of spans), enough items to fill the GPU, each
 // reading the head's row statistics and streaming its chunks' U rows with
-// eight 16-byte loads in flight per thread.  The row sums follow the fixed
+// eight 16-byte loads in flight per thread.  When every head's span
+// statistics are small (at most 32 KB: one round of loads at 128 rows), each
+// combine block forms its head's row statistics itself and the row_lse
+// launch is skipped.  The row sums follow the fixed
 // order of combine_chunks: results are deterministic.
 #include "lse_combine.h"
 
@@ -25,7 +28,8 @@ constexpr int kWeightFloats = 16384;  // weights of one item's spans (64 KB at m
 
 template <int QPT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
-  // dynamic LDS: weights [spans_per_blk][R_pad]
+  // dynamic LDS: weights [spans_per_blk][R_pad], then (fuse_lse) the row
+  // statistics [R_pad] as float2
   extern __shared__ float wts[];
   const int tid = threadIdx.x;
 
@@ -44,12 +48,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
   const float2* lse_g = P.lse + li * P.lse_layer_stride + P.lse_off[b] + static_cast<int64_t>(h) * P.R_pad;
   const int s_lo = blk * P.spans_per_blk;
   const int ns = min(P.spans_per_blk, nspan - s_lo);
-  // the row statistics and the spans' maxima are read together (one memory
-  // round trip before the weights)
-  for (int e = tid; e < ns * P.R_pad; e += kThreads) {
-    const int s = e / P.R_pad, r = e - s * P.R_pad;
-    wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse_g[r], P.scale)
-                     : 0.0f;
+  if (P.fuse_lse) {
+    // short heads: the row statistics are formed here (the same function and
+    // thread count as row_lse_kernel, so the same bits) into LDS after the weights
+    float2* lse_l = reinterpret_cast<float2*>(wts + P.spans_per_blk * P.R_pad);
+    rows_lse<kThreads>(st, nspan, P.R, P.R_pad, P.scale, lse_l);
+    __syncthreads();
+    for (int e = tid; e < ns * P.R_pad; e += kThreads) {
+      const int s = e / P.R_pad, r = e - s * P.R_pad;
+      wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse_l[r], P.scale)
+                       : 0.0f;
+    }
+  } else {
+    // the row statistics and the spans' maxima are read together (one memory
+    // round trip before the weights)
+    for (int e = tid; e < ns * P.R_pad; e += kThreads) {
+      const int s = e / P.R_pad, r = e - s * P.R_pad;
+      wts[e] = r < P.R ? span_weight(st[static_cast<int64_t>(s_lo + s) * P.R_pad + r].x, lse_g[r], P.scale)
+                       : 0.0f;
+    }
   }
   __syncthreads();
 
@@ -89,7 +106,8 @@ int combine_spans_per_blk(int R_pad) {
 
 hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
   if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
-  const size_t lds = static_cast<size_t>(p.spans_per_blk) * p.R_pad * sizeof(float);
+  const size_t lds = static_cast<size_t>(p.spans_per_blk) * p.R_pad * sizeof(float) +
+                    (p.fuse_lse ? static_cast<size_t>(p.R_pad) * sizeof(float2) : 0);
   switch (combine_qpt(p.R_pad)) {
     case 1: return launch1(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p);
     case 2: return launch1(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p);
