@@ -151,6 +151,50 @@ def test_ragged_batch_and_many_sequences():
     _all_units(case)
 
 
+def _draw_problem(seed):
+    """A seeded random problem: dtype, head_dim, GQA shape, window, chunk size
+    (MFMA-supported or not), ragged sequences, budgets from 0 to above T, layer
+    count and reuse interval; sizes bounded so the oracle takes about a second."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ck.BF16 if rng.random() < 0.75 else ck.F32
+    if dtype == ck.BF16:
+        d = 128 if rng.random() < 0.7 else int(rng.choice([8, 64, 96, 256]))
+    else:
+        d = int(rng.choice([8, 32, 64, 100]))   # rows of 32..400 bytes (head_dim >= 8)
+    Hkv = int(rng.choice([1, 2, 3, 8]))
+    G = int(rng.choice([1, 2, 4, 5]))
+    w = int(rng.integers(1, 49))
+    while G * w > 192:
+        w //= 2
+    c = int(rng.choice([1, 2, 3, 4, 5, 7, 10, 11, 16, 20, 33, 64, 100]))
+    B = int(rng.integers(1, 4))
+    lens = [int(rng.integers(w, 6001)) for _ in range(B)]
+    n_layers = int(rng.integers(1, 5))
+    n_reuse = int(rng.integers(1, 4))
+    anchors = -(-n_layers // n_reuse)
+    # oracle work: anchors x sum(T) x Hkv x G*w x d multiply-adds
+    budget = 1e9
+    cost = anchors * sum(lens) * Hkv * G * w * d
+    if cost > budget:
+        f = budget / cost
+        lens = [max(w, int(t * f)) for t in lens]
+    lmax = []
+    for t in lens:
+        u = rng.random()
+        lmax.append(0 if u < 0.15 else t if u < 0.3 else int(rng.integers(0, t + 50)))
+    return dict(dtype=dtype, d=d, Hq=G * Hkv, Hkv=Hkv, w=w, c=c, lens=lens, lmax=lmax,
+                n_layers=n_layers, n_reuse=n_reuse)
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_problems(seed):
+    p = _draw_problem(seed)
+    print("problem", p, flush=True)
+    case = random_case(p["dtype"], p["lens"], p["lmax"], p["Hq"], p["Hkv"], p["d"], p["w"], p["c"],
+                       n_layers=p["n_layers"], n_reuse=p["n_reuse"], seed=seed).run()
+    _all_units(case)
+
+
 @pytest.mark.parametrize("n_reuse", [1, 2, 3, 9])
 def test_layer_index_reuse(n_reuse):
     # Algorithm 2: anchor layers score, the others gather their own K/V with
