@@ -437,7 +437,8 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
         }
       }
       // schedule: the first kLdsAhead fragment reads, then per MFMA: its
-      // key load (every kLoadEvery-th), the MFMA, the fragment read kLdsAhead ahead
+      // key load (every kLoadEvery-th), the MFMA, the fragment read kLdsAhead
+      // ahead (group masks: 0x008 MFMA, 0x020 vector-memory read, 0x100 LDS read)
       __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
 #pragma unroll
       for (int mi = 0; mi < G::NT * kKSteps; ++mi) {
