@@ -269,7 +269,8 @@ def main():
         "wall_s_timed": wall,
     }
     # context outside the timed region: the 8-layer slice (its first 8
-    # layers: 4 scoring + 4 reusing) and a plain device copy of 1 GiB
+    # layers: 4 scoring + 4 reusing), per-phase durations and a plain device
+    # copy of 1 GiB
     extra = {}
     if args.context == "on" and L > 8:
         def slice8():
@@ -286,6 +287,25 @@ def main():
         ms8 = start.elapsed_time(stop) / args.steps
         extra["slice_8_layers"] = {"ms_per_call": ms8, "value": 8 * sum(wl.seq_lens) / (ms8 * 1e-3),
                                    "unit": "layer-tokens/s"}
+    if args.context == "on":
+        # per-phase durations from separate steps that take all four phase
+        # events (score | combine + select | gather); the extra events cost a
+        # few microseconds per step, so these steps are not the timed ones
+        evs_all = [ck.PhaseEvents() for _ in range(args.steps)]
+        for e_all in evs_all:
+            step(e_all)
+        torch.cuda.synchronize()
+
+        def mean_all(i, j):
+            return sum(x.elapsed_ms(i, j) for x in evs_all) / len(evs_all)
+
+        g_bytes = accounting.gather_bytes(kept_total, wl.head_dim, e)
+        g_ms = mean_all(2, 3)
+        g_gbps = g_bytes / (g_ms * 1e-3) / 1e9
+        extra["phase_breakdown"] = {
+            "score_ms": mean_all(0, 1), "combine_select_ms": mean_all(1, 2), "gather_ms": g_ms,
+            "gather_hbm": {"achieved": g_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": g_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": g_bytes}}
     n_copy = 1 << 30 if args.context == "on" else 0
     if n_copy:
         extra["copy_peak"] = copy_peak(n_copy, start, stop, step_gbps)
