@@ -118,6 +118,29 @@ def copy_peak(n: int, start, stop, step_gbps: float, reps: int = 5):
             "step_hbm_frac": step_gbps / gbps}
 
 
+def selection_overlap(bufs, wl, n_reuse, plan):
+    """Mean Jaccard index of the chunk sets selected by consecutive scoring
+    layers (sequence 0, every KV head), from the indices the library wrote;
+    a chunk counts as selected when one of its tokens before the recent
+    window is kept."""
+    import numpy as np
+    T, c, w, H = wl.seq_lens[0], wl.chunk, wl.window, wl.n_kv_heads
+    n_anchor = bufs.n_anchor
+    idx = bufs.indices.view(n_anchor, -1).cpu().numpy()
+    lens = bufs.lengths.view(n_anchor, -1).cpu().numpy()
+    L_cap, off = plan["l_cap"][0], plan["index_off"][0]
+
+    def chunks(a, h):
+        kept = idx[a, off + h * L_cap: off + h * L_cap + lens[a, h]]
+        return set((kept[kept < T - w] // c).tolist())
+
+    sets = [[chunks(a, h) for h in range(H)] for a in range(n_anchor)]
+    jac = [len(sets[a][h] & sets[a + 1][h]) / max(1, len(sets[a][h] | sets[a + 1][h]))
+           for a in range(n_anchor - 1) for h in range(H)]
+    return {"mean_jaccard": float(np.mean(jac)) if jac else None,
+            "pairs": f"scoring layers l and l + {n_reuse}, sequence 0, all {H} KV heads"}
+
+
 def cpu_baseline(wl, cache, n_pairs: int):
     """Time the CPU oracle, as it stands, on a bounded sample: the first
     n_pairs (anchor layer, reusing layer) pairs of sequence 0, every KV head,
@@ -149,10 +172,25 @@ def cpu_baseline(wl, cache, n_pairs: int):
         list(ex.map(unit, jobs))
     dt = time.perf_counter() - t0
     layer_tokens = len(layers) * T
+    # one thread: the first two units of the same sample, one after the other
+    n1 = min(2, len(jobs))
+    t1 = time.perf_counter()
+    for job in jobs[:n1]:
+        unit(job)
+    dt1 = time.perf_counter() - t1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": layer_tokens / dt, "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"layers {layers} of sequence 0 (T={T}), all {wl.n_kv_heads} KV heads: "
                        f"fp64 scoring + full-sort top-k + index build on the scoring layers, "
-                       f"row copies on all; {dt:.2f} s wall")}
+                       f"row copies on all; {dt:.2f} s wall"),
+            "single_thread": {"value": layer_tokens * n1 / len(jobs) / dt1, "unit": "layer-tokens/s",
+                              "sample": f"{n1} of the {len(jobs)} (layer pair, KV head) units, {dt1:.2f} s"},
+            "host": {"cpu_model": model, "logical_cpus": os.cpu_count()}}
 
 
 def main():
@@ -288,6 +326,10 @@ def main():
         extra["slice_8_layers"] = {"ms_per_call": ms8, "value": 8 * sum(wl.seq_lens) / (ms8 * 1e-3),
                                    "unit": "layer-tokens/s"}
     if args.context == "on":
+        # workload diagnostic: overlap of the chunks selected by consecutive
+        # scoring layers (the synthetic caches share 80% of the planted hot
+        # chunks between adjacent layers), mean Jaccard index over the heads
+        extra["selection_overlap"] = selection_overlap(bufs, wl, n_reuse, ck.plan(prob))
         # per-phase durations from separate steps that take all four phase
         # events (score | combine + select | gather); the extra events cost a
         # few microseconds per step, so these steps are not the timed ones
