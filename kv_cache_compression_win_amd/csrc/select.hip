@@ -19,13 +19,14 @@
 // of selected chunks before j_w.
 //
 // Two kernels, one workgroup per (scoring layer, sequence, KV head):
-//   select_fast_kernel  512 threads, C <= 16384: scores in registers
-//     (chunk j in slot j / 512 of thread j % 512), counts by wave ballots,
+//   select_fast_kernel  512 threads for C <= 16384, 1024 threads for
+//     C <= 32768 (token-level chunks of long sequences): scores in registers
+//     (chunk j in slot j / NTH of thread j % NTH), counts by wave ballots,
 //     one barrier per greedy step, the selected ids compacted into LDS and
 //     the index list written position-parallel (coalesced).
-//   select_kernel       1024 threads, any C: scores in registers up to
-//     16384 chunks, else re-read from memory; one exclusive scan per tile
-//     of 1024 chunks places every kept token.
+//   select_kernel       1024 threads, any C: scores re-read from memory
+//     above 32768 chunks; one exclusive scan per tile of 1024 chunks places
+//     every kept token.
 #include <algorithm>
 
 #include "chunkkv_internal.h"
@@ -235,7 +236,9 @@ constexpr int kFastThreads = CKV_SELECT_THREADS;
 constexpr int kFastWaves = kFastThreads / 64;
 constexpr int kFastMaxKPT = 256 / kFastWaves;   // (slot, wave) tables of at most 256 entries
 constexpr int kFastMaxChunks = kFastThreads * kFastMaxKPT;
-constexpr int kFastTable = kFastMaxKPT * kFastWaves;
+// 1024 threads with 32 scores each: C <= 32768 (token-level chunks of long sequences)
+constexpr int kWideThreads = 1024;
+constexpr int kWideMaxChunks = kWideThreads * 32;
 
 __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
 
@@ -245,17 +248,21 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
 }
 
-// Exclusive prefix sum, in place, of tab[0 .. E) (E <= 256) by wave 0, four
-// consecutive entries per lane; tab[E] receives the total.  Callers barrier
-// before and after.
+// Exclusive prefix sum, in place, of tab[0 .. E) (E <= 64 * EPL) by wave 0,
+// EPL consecutive entries per lane; tab[E] receives the total.  Callers
+// barrier before and after.
+template <int EPL>
 __device__ __forceinline__ void wave0_scan_table(int* tab, int E) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  const int e0 = 4 * lane;
-  int a[4];
+  const int e0 = EPL * lane;
+  int a[EPL];
+  int own = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = e0 + i < E ? tab[e0 + i] : 0;
-  const int own = a[0] + a[1] + a[2] + a[3];
+  for (int i = 0; i < EPL; ++i) {
+    a[i] = e0 + i < E ? tab[e0 + i] : 0;
+    own += a[i];
+  }
   int x = own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -264,19 +271,22 @@ __device__ __forceinline__ void wave0_scan_table(int* tab, int E) {
   }
   int base = x - own;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     if (e0 + i < E) tab[e0 + i] = base;
     base += a[i];
   }
   if (lane == 63) tab[E] = x;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectParams P) {
+template <int KPT, int NTH>
+__global__ __launch_bounds__(NTH) void select_fast_kernel(const SelectParams P) {
+  constexpr int kFastThreads = NTH, kFastWaves = NTH / 64;
+  constexpr int kEPL = (KPT * kFastWaves + 63) / 64;   // table entries per lane of the wave-0 scans
+  static_assert(kEPL <= 8, "(slot, wave) tables of at most 512 entries");
   extern __shared__ int sel_ids[];                  // selected chunk ids < j_w, ascending
   __shared__ int4 red[2][kFastWaves];
-  __shared__ int eq_tab[kFastTable + 1];
-  __shared__ int sel_tab[kFastTable + 1];
+  __shared__ int eq_tab[KPT * kFastWaves + 1];
+  __shared__ int sel_tab[KPT * kFastWaves + 1];
   __shared__ int jw_selected;
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int E = KPT * kFastWaves;               // (slot, wave) table entries
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
     }
     const int4 t = wg_sum(make_int4(gt, 0, 0, 0));   // its barrier also publishes eq_tab
     need = kk - t.x;
-    wave0_scan_table(eq_tab, E);
+    wave0_scan_table<kEPL>(eq_tab, E);
     __syncthreads();
   }
 
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
     sel_tab[i * kFastWaves + wave] = __popcll(pre[i]);
   }
   __syncthreads();
-  wave0_scan_table(sel_tab, E);
+  wave0_scan_table<kEPL>(sel_tab, E);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -419,13 +429,13 @@ __global__ __launch_bounds__(kFastThreads) void select_fast_kernel(const SelectP
   if (tid == 0) P.lengths[li * P.len_layer_stride + P.len_off[b] + h] = n;
 }
 
-template <int KPT>
+template <int KPT, int NTH = kFastThreads>
 hipError_t launch_fast(const SelectParams& p, int n_blocks, hipStream_t s) {
   // LDS for the selected chunk ids: exactly min(k, C) chunks are selected
   int sel_max = 1;
   for (int b = 0; b < p.n_seqs; ++b) sel_max = std::max(sel_max, std::min(p.kk[b], p.C[b]));
   const size_t lds = static_cast<size_t>(sel_max) * sizeof(int);
-  return launch1(select_fast_kernel<KPT>, dim3(n_blocks), dim3(kFastThreads), lds, s, p);
+  return launch1(select_fast_kernel<KPT, NTH>, dim3(n_blocks), dim3(NTH), lds, s, p);
 }
 
 }  // namespace
@@ -443,6 +453,7 @@ hipError_t launch_select(const SelectParams& p, int n_blocks, hipStream_t s) {
       if (c_max <= 16 * kFastThreads) return launch_fast<16>(p, n_blocks, s);
     if constexpr (kFastMaxKPT >= 32) return launch_fast<32>(p, n_blocks, s);
   }
+  if (c_max <= kWideMaxChunks) return launch_fast<32, kWideThreads>(p, n_blocks, s);
   return launch1(select_kernel, dim3(n_blocks), dim3(kSelectThreads), 0, s, p);
 }
 

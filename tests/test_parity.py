@@ -101,6 +101,7 @@ def test_mfma_row_blocks(Hq, Hkv, w, c):
     ("single_token_window", 333, 50, 1, 10),
     ("window_plus_one", 33, 10, 32, 10),
     ("one_chunk_left", 75, 70, 5, 10),
+    ("all_of_20000_chunks", 20000, 20000, 16, 1),   # 1024-thread select, every chunk kept
 ])
 def test_edge_cases(name, T, l_max, w, c):
     case = random_case(ck.BF16, [T], [l_max], 8, 2, 128, w, c, seed=T + w).run()
@@ -117,7 +118,8 @@ def test_edge_cases(name, T, l_max, w, c):
 @pytest.mark.parametrize("dtype,d,c,T", [(ck.BF16, 128, 10, 3001), (ck.BF16, 128, 1, 2500),
                                          (ck.F32, 64, 10, 1201), (ck.BF16, 128, 2, 9001),
                                          (ck.BF16, 128, 1, 12000),    # C = 12000: 32 scores per thread
-                                         (ck.BF16, 128, 1, 20000)])   # C = 20000 > 16384: 1024-thread kernel
+                                         (ck.BF16, 128, 1, 20000),    # C = 20000: 1024 threads x 32 scores
+                                         (ck.BF16, 128, 1, 40000)])   # C = 40000 > 32768: scores re-read
 def test_tied_scores_lower_id_first(dtype, d, c, T):
     # all-zero keys: every logit is 0, so every full chunk gets the same score
     # (c/T per row) and only the short last chunk differs; the top-k must take
@@ -422,7 +424,8 @@ def _adversarial_scores(rng, C, with_pos_nan):
 
 @pytest.mark.parametrize("T,c,w,l_max", [(2000, 10, 16, 300),       # register path (C = 200)
                                          (90001, 10, 32, 9000),     # C = 9001: 32 scores per thread
-                                         (200001, 10, 32, 20000)])  # C = 20001 > 16384: 1024-thread kernel
+                                         (200001, 10, 32, 20000),   # C = 20001: 1024 threads x 32 scores
+                                         (400001, 10, 32, 40000)])  # C = 40001 > 32768: scores re-read
 def test_select_any_scores_stays_in_range(T, c, w, l_max):
     # chunkkv_select takes caller scores: a score with the sign bit set counts
     # as 0 and the rest are ordered by bit pattern, so exactly k chunks are
