@@ -135,7 +135,10 @@ size_t chunkkv_workspace_bytes(const chunkkv_problem *p, int32_t n_score_layers)
 /*
  * Algorithm 1 steps 1-3 (ChunkKV page, section 4.1) with Kara eq. (1):
  * observe-window attention of every (sequence, KV head), summed into the
- * C_b chunk scores.
+ * C_b chunk scores.  bf16 caches with head_dim 128 and c <= 3 whose G*w rows
+ * fit one 128-row block are scored in two passes over the keys (row
+ * statistics, then the final scores) instead of through per-row chunk
+ * partials; the workspace is sized for whichever path the problem takes.
  *   q_win     DEVICE window queries (layout in chunkkv_problem)
  *   k         DEVICE keys (layout in chunkkv_problem)
  *   scores    DEVICE fp32 out, scores_elems entries (layout: chunkkv_sizes)
@@ -196,8 +199,9 @@ int chunkkv_gather(const chunkkv_problem *p, const void *k, const void *v,
  *                   its end, the start of the gather phase and its end (for
  *                   timing; any entry may be NULL).  A phase that is a
  *                   single kernel launch (the bf16 d=128 score kernel over
- *                   every scoring layer; the gather over at most 32 layers;
- *                   at most 8 sequences) takes its two events at that
+ *                   every scoring layer, unless the problem is scored in two
+ *                   passes; the gather over at most 32 layers; at most 8
+ *                   sequences) takes its two events at that
  *                   kernel's own start and end (hipExtLaunchKernel);
  *                   otherwise they are recorded between the phases'
  *                   kernels.  When the

@@ -58,6 +58,7 @@ struct Plan {
   int dtype = 0, eb = 0, B = 0, Hq = 0, Hkv = 0, G = 0, d = 0, w = 0, c = 0;
   int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
   bool mfma = false;
+  bool two_pass = false;   // statistics pass + final-score pass, no chunk partials
   std::vector<Seq> seq;
   int64_t scores_elems = 0, index_elems = 0, length_elems = 0, u_elems = 0, st_elems = 0, lse_elems = 0;
   int64_t kv_st = 0, kv_sh = 0, q_ss = 0, q_sr = 0, q_sh = 0;
@@ -116,6 +117,10 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   pl.R_pad = static_cast<int>(pl.mfma ? round_up(R, kMfmaRows) : round_up(R, 4));
   pl.n_rb = pl.mfma ? pl.R_pad / kMfmaRows : 1;
   pl.span_chunks = pl.mfma ? score_mfma_span_chunks(pl.c) : score_generic_span_chunks(pl.R_pad, pl.c);
+  // short chunks with one row block: the chunk partials (4*R_pad/c bytes
+  // per key token and head, written and read back) would outweigh a second
+  // pass over the keys (2*d bytes)
+  pl.two_pass = pl.mfma && pl.n_rb == 1 && score_two_pass_supported(pl.c);
   pl.kv_st = p->kv_stride_tok;
   pl.kv_sh = p->kv_stride_head;
   pl.q_ss = p->q_stride_seq;
@@ -146,7 +151,7 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     s.lse_off = pl.lse_elems;
     pl.scores_elems += static_cast<int64_t>(pl.Hkv) * s.C;
     pl.index_elems += static_cast<int64_t>(pl.Hkv) * s.L_cap;
-    pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * pl.R_pad;
+    if (!pl.two_pass) pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * pl.R_pad;
     pl.st_elems += static_cast<int64_t>(pl.Hkv) * s.n_span * pl.R_pad;
     pl.lse_elems += static_cast<int64_t>(pl.Hkv) * pl.R_pad;
     items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * s.n_span;
@@ -161,9 +166,12 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
 // ------------------------------------------------------------- launchers --
 
 // ev_start / ev_stop (null, or only with one sequence batch and the MFMA
-// kernel) are recorded at the score kernel's start and end.
+// kernel) are recorded at the score kernel's start and end.  mode is
+// kScorePartials (U and statistics), kScoreStats (statistics only) or
+// kScoreFinal (chunk scores from the row statistics lse).
 hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U,
-                     float2* st, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+                     float2* st, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                     int mode = kScorePartials, const float2* lse = nullptr, float* scores = nullptr) {
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
     ScoreParams P{};
@@ -185,14 +193,21 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
       P.item0[i] = items;
       P.u_off[i] = sq.u_off;
       P.st_off[i] = sq.st_off;
+      P.s_off[i] = sq.score_off;
+      P.lse_off[i] = sq.lse_off;
       items += pl.Hkv * pl.n_rb * sq.n_span;
     }
     P.item0[nb] = items;
     P.items_per_layer = items;
     P.u_layer_stride = pl.u_elems;
     P.st_layer_stride = pl.st_elems;
+    P.s_layer_stride = pl.scores_elems;
+    P.lse_layer_stride = pl.lse_elems;
     P.U = U;
     P.stats = st;
+    P.mode = mode;
+    P.S = scores;
+    P.lse = lse;
     P.H_q = pl.Hq;
     P.H_kv = pl.Hkv;
     P.G = pl.G;
@@ -223,8 +238,9 @@ constexpr int64_t kCombineMinBlocks = 512;
 
 constexpr int64_t kFuseLseBytes = 32768;
 
+// lse_only: the row statistics alone (the two-pass path's final pass reads them).
 hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
-                       hipStream_t s) {
+                       hipStream_t s, bool lse_only = false) {
   // spans per combine block: fewer when the launch would otherwise have too
   // few blocks to spread over the GPU (a layer or two of short sequences)
   int spb = combine_spans_per_blk(pl.R_pad);
@@ -276,13 +292,29 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
     // more spans the repeated reads cost more than the launch (32k layers)
     int64_t st_bytes = 0;
     for (int i = 0; i < nb; ++i) st_bytes = std::max<int64_t>(st_bytes, int64_t{8} * P.n_span[i] * pl.R_pad);
-    P.fuse_lse = st_bytes <= kFuseLseBytes ? 1 : 0;
+    P.fuse_lse = st_bytes <= kFuseLseBytes && !lse_only ? 1 : 0;
     hipError_t e = P.fuse_lse ? hipSuccess : launch_row_lse(P, nl * nb * pl.Hkv, s);
     if (e != hipSuccess) return e;
+    if (lse_only) continue;
     e = launch_combine(P, nl * items, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Scores of nl scoring layers: chunk partials then the log-sum-exp combine,
+// or (pl.two_pass) statistics, row statistics and a final pass over the keys.
+hipError_t run_scores(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U, float2* st,
+                      float2* lse, float* scores, hipStream_t s, hipEvent_t ev_start = nullptr,
+                      hipEvent_t ev_stop = nullptr) {
+  hipError_t e;
+  if (!pl.two_pass) {
+    if ((e = run_score(pl, nl, q, k, U, st, s, ev_start, ev_stop)) != hipSuccess) return e;
+    return run_combine(pl, nl, U, st, lse, scores, s);
+  }
+  if ((e = run_score(pl, nl, q, k, U, st, s, nullptr, nullptr, kScoreStats)) != hipSuccess) return e;
+  if ((e = run_combine(pl, nl, U, st, lse, scores, s, true)) != hipSuccess) return e;
+  return run_score(pl, nl, q, k, U, st, s, nullptr, nullptr, kScoreFinal, lse, scores);
 }
 
 hipError_t run_select(const Plan& pl, int nl, const float* scores, int32_t* indices, int32_t* lengths,
@@ -421,10 +453,8 @@ int chunkkv_score(const chunkkv_problem* p, const void* q_win, const void* k, fl
   float* U;
   float2 *st, *lse;
   carve(pl, 1, workspace, &U, &st, &lse);
-  hipError_t e = run_score(pl, 1, &q_win, &k, U, st, s);
+  hipError_t e = run_scores(pl, 1, &q_win, &k, U, st, lse, scores, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
-  e = run_combine(pl, 1, U, st, lse, scores, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
 
@@ -490,7 +520,7 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
   const bool one_batch = n_anchor <= batch;
   // a phase that is one kernel launch takes its events at that kernel's start
   // and end (no separate stream markers between the kernels of a step)
-  const bool score_events = one_batch && pl.mfma && pl.B <= kMaxSeqs;
+  const bool score_events = one_batch && pl.mfma && !pl.two_pass && pl.B <= kMaxSeqs;
   const bool gather_events = n_layers <= kMaxLayers && pl.B <= kMaxSeqs;
   hipError_t e = score_events ? hipSuccess : record(0);
   if (e != hipSuccess) return hip_fail(e, "phase event");
@@ -506,12 +536,18 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
       qb[i] = q_win[(a0 + i) * n_reuse];
       kb[i] = k[(a0 + i) * n_reuse];
     }
-    if ((e = score_events ? run_score(pl, na, qb, kb, U, st, s, ev(0), ev(1)) : run_score(pl, na, qb, kb, U, st, s)) !=
-        hipSuccess)
-      return hip_fail(e, "score launch");
-    if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-    if ((e = run_combine(pl, na, U, st, lse, scores + a0 * pl.scores_elems, s)) != hipSuccess)
-      return hip_fail(e, "combine launch");
+    float* sc = scores + a0 * pl.scores_elems;
+    if (pl.two_pass) {
+      // statistics pass, row statistics and final pass: the score phase
+      if ((e = run_scores(pl, na, qb, kb, U, st, lse, sc, s)) != hipSuccess) return hip_fail(e, "score launch");
+      if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
+    } else {
+      if ((e = score_events ? run_score(pl, na, qb, kb, U, st, s, ev(0), ev(1))
+                            : run_score(pl, na, qb, kb, U, st, s)) != hipSuccess)
+        return hip_fail(e, "score launch");
+      if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
+      if ((e = run_combine(pl, na, U, st, lse, sc, s)) != hipSuccess) return hip_fail(e, "combine launch");
+    }
     if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
                         lengths + a0 * pl.length_elems, s)) != hipSuccess)
       return hip_fail(e, "select launch");

@@ -43,11 +43,18 @@ constexpr float kRebaseLog2 = 64.0f;
 // ----------------------------------------------------------------- score --
 // One launch scores up to kMaxLayers layers x kMaxSeqs sequences.  Work item
 // = (layer, sequence b, KV head h, row block rb, span s); a span is a run of
-// span_chunks whole chunks.  Each item writes
+// span_chunks whole chunks.  In mode kScorePartials each item writes
 //   U[layer][u_off[b] + (h*C_b + j)*R_pad + r]      chunk partials
 //   stats[layer][st_off[b] + (h*n_span_b + s)*R_pad + r] = (m_ref, l)
 // where U is sum over the chunk's tokens of exp2((x - m_ref)*scale) and l
-// is sum over the span of the same terms.
+// is sum over the span of the same terms.  Short chunks (two passes over the
+// keys, one row block): mode kScoreStats writes the statistics only, and
+// after the row statistics (M_r, L_r) exist, mode kScoreFinal writes
+//   S[layer][s_off[b] + h*C_b + j] = sum_r sum_{t in j} 2^((x - M_r)*scale) / L_r.
+constexpr int kScorePartials = 0;
+constexpr int kScoreStats = 1;
+constexpr int kScoreFinal = 2;
+
 struct ScoreParams {
   const void* q[kMaxLayers];
   const void* k[kMaxLayers];
@@ -75,6 +82,12 @@ struct ScoreParams {
   int64_t st_layer_stride;
   float* U;
   float2* stats;
+  int32_t mode;                 // kScorePartials, kScoreStats or kScoreFinal
+  float* S;                     // kScoreFinal: chunk scores
+  const float2* lse;            // kScoreFinal: row statistics (M_r, L_r), [H_kv][R_pad] per sequence
+  int64_t s_off[kMaxSeqs];
+  int64_t lse_off[kMaxSeqs];
+  int64_t s_layer_stride, lse_layer_stride;
   int32_t H_q, H_kv, G, w, c, d, R, R_pad, n_rb;
   int64_t kv_st, kv_sh, q_ss, q_sr, q_sh;
   float scale;                  // log2(e) / sqrt(d)
@@ -164,6 +177,8 @@ struct GatherParams {
 // Host-side launchers (defined next to their kernels).
 // MFMA path: bf16, head_dim 128, chunk size with a static layout.
 bool score_mfma_supported(int chunk);
+// Chunk sizes with the two-pass kernels (statistics, then final scores).
+bool score_two_pass_supported(int chunk);
 int score_mfma_span_chunks(int chunk);
 // Launches min(n_items, resident workgroups) persistent workgroups.
 // Launches `kernel` with one by-value argument and returns the launch's own

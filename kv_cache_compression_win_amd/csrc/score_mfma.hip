@@ -15,6 +15,14 @@
 // kernel writes, per query row, the chunk partials
 //   U[j][r] = sum_{t in chunk j} 2^((x_rt - m_r) * log2(e)/sqrt(d))
 // and (m_r, l_r = sum over the span) for the log-sum-exp combine.
+//
+// Short chunks (c <= 3) with one 128-row block per head take two passes over
+// the keys instead, since their partials U (one float per row and chunk)
+// would outweigh the keys: the first pass writes only the span statistics;
+// after the row statistics (M_r, L_r) are formed, the second computes each
+// logit's final probability 2^((x - M_r)*scale - log2 L_r), sums it per chunk
+// in registers and over the block's 128 rows through LDS, and writes the
+// chunk scores themselves.
 #include <type_traits>
 
 #include "chunkkv_internal.h"
@@ -41,6 +49,11 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kKeysOnce = 2;
 constexpr int kKeysShared = 0;
 constexpr int kSharedKeySpans = 8;
+// Chunk sizes scored in two passes over the keys (statistics, then final
+// scores) when a head has one row block: there the chunk partials U
+// (4*R_pad/c bytes per key token and head, written and read back) would
+// outweigh a second read of the keys (2*d bytes).
+constexpr int kTwoPassMaxChunk = 3;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 constexpr int kLdsAhead = 4;         // key fragment reads issued ahead of their MFMA
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
@@ -107,7 +120,7 @@ __device__ __forceinline__ float chunk_exp_sum(const f32x16 (&acc)[Geo<CC>::NT],
 // or is not finite (always the case on a span's first group, where m_ref is
 // -inf): without it, every term is below 2^64 and the test would fail anyway.
 // Slots past the end of the sequence are masked to -inf (exp2 gives 0).
-template <int CC>
+template <int CC, bool STORE>
 __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool full, int nvalid,
                                               float scale, float rebase_raw, float& m_ref,
                                               float& l_acc, float* u_row, int gi) {
@@ -138,9 +151,10 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
     mx = fmaxf(mx, shfl_xor32(mx));
     if (mx > m_ref + rebase_raw) {
       const float f = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mx) * scale);
-      for (int gg = 0; gg < gi; ++gg)
+      if constexpr (STORE)
+        for (int gg = 0; gg < gi; ++gg)
 #pragma unroll
-        for (int q = 0; q < G::CPH; ++q) u_row[(gg * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
+          for (int q = 0; q < G::CPH; ++q) u_row[(gg * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
       l_acc *= f;
       m_ref = mx;
 #pragma unroll
@@ -150,9 +164,58 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
   float* dst = u_row + gi * G::GROUP_CHUNKS * kMfmaRows;
 #pragma unroll
   for (int q = 0; q < G::CPH; ++q) {
-    dst[q * kMfmaRows] = u[q];
+    if constexpr (STORE) dst[q * kMfmaRows] = u[q];
     l_acc += u[q];
   }
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Row stride (floats) of the per-wave transpose buffer of the final pass:
+// 16-byte aligned rows whose 16-byte reads by 16 consecutive lanes fall in
+// distinct banks.
+constexpr int kRedStride = 36;
+
+// Final pass, one group: this lane's row probabilities summed per chunk
+// (exp2((x - M_r)*scale - log2 L_r), nfin = -(M_r*scale + log2 L_r), -inf for
+// padding rows), then summed over the wave's 32 rows through LDS: chunk q of
+// lane half ho goes to row (ho*CPH + q) of `red`, column n; lanes then add
+// their chunk's 16-row half in row order and the two halves meet by one
+// cross-half exchange.  Lane l < GROUP_CHUNKS writes chunk l's sum to s_row[l].
+template <int CC>
+__device__ __forceinline__ void group_final(f32x16 (&acc)[Geo<CC>::NT], bool full, int nvalid, float scale,
+                                            float nfin, float* red, float* s_row, int lane, int n, int ho) {
+  using G = Geo<CC>;
+  static_assert(G::GROUP_CHUNKS <= 32, "final pass: one lane per chunk of a group");
+  if (!full) {
+#pragma unroll
+    for (int tau = 0; tau < G::NT; ++tau)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lam = 16 * tau + v;
+        if (lam < G::HALF_TOK) acc[tau][v] = lam < nvalid ? acc[tau][v] : -INFINITY;
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < G::CPH; ++q) red[(ho * G::CPH + q) * kRedStride + n] = chunk_exp_sum<CC>(acc, q, scale, nfin);
+  wave_sync();
+  const int cl = lane & 31, rh = lane >> 5;
+  float sum = 0.0f;
+  if (cl < G::GROUP_CHUNKS) {
+    const float4* p = reinterpret_cast<const float4*>(red + cl * kRedStride + 16 * rh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = p[i];
+      sum += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+  sum += shfl_xor32(sum);
+  if (lane < G::GROUP_CHUNKS) s_row[lane] = sum;
+  wave_sync();
 }
 
 // One work item: (layer, sequence, KV head, row block, span of whole chunks).
@@ -179,6 +242,8 @@ struct Tables {
   int64_t tok0[kMaxSeqs];
   int64_t u_off[kMaxSeqs];
   int64_t st_off[kMaxSeqs];
+  int64_t s_off[kMaxSeqs];
+  int64_t lse_off[kMaxSeqs];
   int32_t item0[kMaxSeqs + 1];
   int32_t n_span[kMaxSeqs];
   int32_t T[kMaxSeqs];
@@ -198,6 +263,8 @@ __device__ __forceinline__ void load_tables(const ScoreParams& P, Tables& t) {
     t.tok0[i] = P.tok0[i];
     t.u_off[i] = P.u_off[i];
     t.st_off[i] = P.st_off[i];
+    t.s_off[i] = P.s_off[i];
+    t.lse_off[i] = P.lse_off[i];
     t.n_span[i] = P.n_span[i];
     t.T[i] = P.T[i];
     t.C[i] = P.C[i];
@@ -258,7 +325,7 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 // groups k+1 .. k+STAGES-1 -- of this item or the next ones -- are in flight.
 // The ring is indexed statically (the loop is unrolled by STAGES), so each
 // LDS store waits only for the loads of its own stage.
-template <int CC, int KAUX>
+template <int CC, int KAUX, int MODE>
 __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
   using G = Geo<CC>;
   constexpr int kLoadEvery = G::NT * kKSteps / G::LOADS;   // MFMAs per key load of the next group
@@ -346,7 +413,29 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   // stores go through buffer resources sized to the data (pieces past the
   // span's last chunk are dropped), so their number is fixed: the compiler's
   // memory-counter waits in the main loop then stay exact.
+  // final pass: per-wave transpose buffers, then the span's per-wave chunk sums
+  float* const red = u_lds + wave * (G::GROUP_CHUNKS * kRedStride);
+  float* const s_lds = u_lds + 4 * G::GROUP_CHUNKS * kRedStride;   // [4 waves][SPAN_CHUNKS]
+  static_assert(MODE != kScoreFinal ||
+                    4 * G::GROUP_CHUNKS * kRedStride + 4 * G::SPAN_CHUNKS <= G::SPAN_CHUNKS * kMfmaRows,
+                "final-pass buffers fit in the partials' LDS");
   auto flush = [&](const Item& it, float m_ref, float l_acc) {
+    if constexpr (MODE == kScoreFinal) {
+      // the span's chunk scores: the 4 waves' row sums added in wave order;
+      // every thread issues one store, those past the span's chunks are dropped
+      __syncthreads();
+      const int nch = sgpr(min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS));
+      const uint64_t sb = reinterpret_cast<uint64_t>(P.S + it.li * P.s_layer_stride) +
+                          4 * static_cast<uint64_t>(sgpr64(tab.s_off[it.b]) + static_cast<int64_t>(it.h) * it.C +
+                                                    it.span * G::SPAN_CHUNKS);
+      const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(sgpr64(sb)), 0, nch * 4, kBufferWord3);
+      const int j = min(tid, G::SPAN_CHUNKS - 1);
+      const float v = (s_lds[j] + s_lds[G::SPAN_CHUNKS + j]) +
+                      (s_lds[2 * G::SPAN_CHUNKS + j] + s_lds[3 * G::SPAN_CHUNKS + j]);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsS, tid * 4, 0, 0);
+      return;
+    }
     const float l_row = l_acc + shfl_xor32(l_acc);
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const uint64_t sbase = reinterpret_cast<uint64_t>(P.stats + it.li * P.st_layer_stride) +
@@ -358,6 +447,7 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     // both lane halves hold the row's statistics; half 1 aims past the end
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_ref), __float_as_uint(l_row)}, rs,
                                           (wave * 32 + n) * 8 + ho * kMfmaRows * 8, 0, 0);
+    if constexpr (MODE == kScoreStats) return;
     __syncthreads();
     const int nch = sgpr(min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS));
     const uint64_t ubase = reinterpret_cast<uint64_t>(P.U + it.li * P.u_layer_stride) +
@@ -397,6 +487,18 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     for (int x = 0; x < G::LOADS; ++x) dst[x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
   };
   load_q(cc.it);
+  // final pass: -(M_r*scale + log2 L_r) of this lane's row (a workgroup's
+  // range lies in one unit), -inf for padding rows
+  float nfin = -INFINITY;
+  if constexpr (MODE == kScoreFinal) {
+    const Item& u0 = cc.it;
+    const int r = u0.rb * kMfmaRows + wave * 32 + n;
+    if (r < P.R) {
+      const float2 ml = P.lse[u0.li * P.lse_layer_stride + sgpr64(tab.lse_off[u0.b]) +
+                              static_cast<int64_t>(u0.h) * P.R_pad + r];
+      nfin = -fmaf(ml.x, P.scale, log2f(ml.y));
+    }
+  }
   // issue the stages strictly in ring order (stage 0 oldest)
 #pragma unroll
   for (int s = 0; s < G::STAGES; ++s) {
@@ -449,8 +551,12 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
       const Item& it = cc.it;
       const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
       const int nvalid = it.tok_end - (gtok0 + ho * G::HALF_TOK);
-      group_softmax<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, P.rebase_raw, m_ref, l_acc,
-                        u_row, cc.g);
+      if constexpr (MODE == kScoreFinal)
+        group_final<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, nfin, red,
+                        s_lds + wave * G::SPAN_CHUNKS + cc.g * G::GROUP_CHUNKS, lane, n, ho);
+      else
+        group_softmax<CC, MODE == kScorePartials>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale,
+                                                  P.rebase_raw, m_ref, l_acc, u_row, cc.g);
       if (cc.g + 1 == it.ngroups) {
         flush(it, m_ref, l_acc);
         m_ref = -INFINITY;
@@ -479,6 +585,8 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
 #define CKV_CHUNKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(15) X(16) X(20) X(25) X(30) X(32) X(40) X(64)
 
 }  // namespace
+
+bool score_two_pass_supported(int chunk) { return chunk >= 1 && chunk <= kTwoPassMaxChunk; }
 
 bool score_mfma_supported(int chunk) {
   switch (chunk) {
@@ -514,7 +622,7 @@ int score_mfma_span_chunks(int chunk) {
 
 // Work split: balanced ranges of consecutive spans of one unit, about one
 // workgroup per resident slot (shorter ranges for heads of several row blocks).
-template <int CC, int KAUX>
+template <int CC, int KAUX, int MODE>
 hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   static thread_local int cached_dev = -1, cached_slots = 0;
   int dev = 0;
@@ -523,7 +631,7 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev
   if (dev != cached_dev) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<CC, KAUX>, kThreads, 0)) !=
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<CC, KAUX, MODE>, kThreads, 0)) !=
         hipSuccess)
       return e;
     cached_dev = dev;
@@ -548,16 +656,28 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev
   p.rb_interleave = p.n_rb > 1 ? 1 : 0;
   for (int b = 0; b < p.n_seqs; ++b)
     if ((p.H_kv * p.wpu[b]) % 8 != 0) p.rb_interleave = 0;
-  return launch1(score_mfma_kernel<CC, KAUX>, dim3(w * p.n_layers), dim3(kThreads), 0, s, p, ev_start, ev_stop);
+  return launch1(score_mfma_kernel<CC, KAUX, MODE>, dim3(w * p.n_layers), dim3(kThreads), 0, s, p, ev_start,
+                 ev_stop);
 }
 
 template <int CC>
 hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if constexpr (pick_tiles(CC) >= 1)
-    return p.n_rb > 1 ? launch_split<CC, kKeysShared>(p, n_items, s, e0, e1)
-                      : launch_split<CC, kKeysOnce>(p, n_items, s, e0, e1);
-  else
+  if constexpr (pick_tiles(CC) >= 1) {
+    if (p.mode != kScorePartials) {
+      // two passes: short chunks, one row block (keys read once per pass)
+      if constexpr (CC <= kTwoPassMaxChunk) {
+        if (p.n_rb != 1) return hipErrorInvalidValue;
+        return p.mode == kScoreStats ? launch_split<CC, kKeysOnce, kScoreStats>(p, n_items, s, e0, e1)
+                                     : launch_split<CC, kKeysOnce, kScoreFinal>(p, n_items, s, e0, e1);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    return p.n_rb > 1 ? launch_split<CC, kKeysShared, kScorePartials>(p, n_items, s, e0, e1)
+                      : launch_split<CC, kKeysOnce, kScorePartials>(p, n_items, s, e0, e1);
+  } else {
     return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {

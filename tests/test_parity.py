@@ -307,10 +307,11 @@ def test_deterministic():
     assert np.array_equal(s1, a.scores) and np.array_equal(i1, a.indices)
 
 
-@pytest.mark.parametrize("dtype,d", [(ck.BF16, 128),    # events on the score and gather kernels
-                                     (ck.F32, 64)])     # events recorded between the phases' kernels
-def test_phase_events(dtype, d):
-    case = random_case(dtype, [4096], [400], 32, 8, d, 32, 10, n_layers=4, n_reuse=2, seed=2)
+@pytest.mark.parametrize("dtype,d,c", [(ck.BF16, 128, 10),    # events on the score and gather kernels
+                                       (ck.F32, 64, 10),      # events recorded between the phases' kernels
+                                       (ck.BF16, 128, 2)])    # two passes over the keys: markers
+def test_phase_events(dtype, d, c):
+    case = random_case(dtype, [4096], [400], 32, 8, d, 32, c, n_layers=4, n_reuse=2, seed=2)
     ev = ck.PhaseEvents()
     case.run(phase_events=ev)
     times = [ev.elapsed_ms(i, i + 1) for i in range(ck.N_PHASE_EVENTS - 1)]
