@@ -118,6 +118,39 @@ def copy_peak(n: int, start, stop, step_gbps: float, reps: int = 5):
             "step_hbm_frac": step_gbps / gbps}
 
 
+def hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args, start, stop):
+    """The hybrid layer policy (ChunkKV page, section 5.7): the lower half of
+    the layers keeps chunk size c, the upper half scores single tokens (c = 1,
+    same L_max and reuse), one compress_layers call per half."""
+    import torch
+    from kv_cache_compression_win_amd import chunkkv as ck
+    L = len(ks)
+    half = (L // 2 // n_reuse) * n_reuse
+    prob1 = ck.make_problem(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                            wl.window, 1)
+    b1 = ck.Buffers(prob1, L - half, n_reuse, wl.head_dim, torch.bfloat16, "cuda")
+    lo = (prob, n_reuse, qs[:half], ks[:half], vs[:half], kos[:half], vos[:half], bufs.scores, bufs.indices,
+          bufs.lengths, bufs.workspace, bufs.ws_bytes)
+    hi = (prob1, n_reuse, qs[half:], ks[half:], vs[half:], list(b1.k_out), list(b1.v_out), b1.scores,
+          b1.indices, b1.lengths, b1.workspace, b1.ws_bytes)
+
+    def call():
+        ck.compress_layers(*lo)
+        ck.compress_layers(*hi)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    return {"layers": f"0-{half - 1} at c = {wl.chunk}, {half}-{L - 1} at c = 1", "ms_per_step": ms,
+            "value": L * sum(wl.seq_lens) / (ms * 1e-3), "unit": "layer-tokens/s"}
+
+
 def selection_overlap(bufs, wl, n_reuse, plan):
     """Mean Jaccard index of the chunk sets selected by consecutive scoring
     layers (sequence 0, every KV head), from the indices the library wrote;
@@ -348,6 +381,9 @@ def main():
             "score_ms": mean_all(0, 1), "combine_select_ms": mean_all(1, 2), "gather_ms": g_ms,
             "gather_hbm": {"achieved": g_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": g_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": g_bytes}}
+    if args.context == "on" and L >= 4 and wl.chunk > 1:
+        extra["hybrid_policy"] = hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args,
+                                               start, stop)
     n_copy = 1 << 30 if args.context == "on" else 0
     if n_copy:
         extra["copy_peak"] = copy_peak(n_copy, start, stop, step_gbps)
