@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.orc_indices.argtypes = [i64, i32, i32, i64, vp, vp]
         L.orc_gather.restype = None
         L.orc_gather.argtypes = [i64, vp, i32, i32, vp, i64, i64, i32, vp]
+        L.orc_decode_attention.restype = i32
+        L.orc_decode_attention.argtypes = [i32, i64, i32, i32, vp, vp, vp, vp]
         L.orc_compress_layers.restype = i32
         L.orc_compress_layers.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, i64,
                                           i32, i32, vp, i64, i64, vp, vp, i64, i64,
@@ -133,6 +135,23 @@ def gather(src: np.ndarray, idx: np.ndarray, head: int) -> np.ndarray:
     dst = np.empty((idx.size, d), dtype=src.dtype)
     lib().orc_gather(idx.size, _ptr(idx), src.itemsize, d, _ptr(src), hkv * d, d, head, _ptr(dst))
     return dst
+
+
+def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Decode attention of the G queries ``q[G, d]`` over one head's kept rows
+    ``k[n, d]``, ``v[n, d]`` (softmax(q . k / sqrt(d)) weights, Kara eq. (1)),
+    float64 [G, d]; zeros when n == 0."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    G, d = q.shape
+    n = k.shape[0]
+    assert k.shape == (n, d) and v.shape == (n, d) and q.dtype == k.dtype == v.dtype
+    out = np.empty((G, d), dtype=np.float64)
+    rc = lib().orc_decode_attention(_dtype_code(k), n, G, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"orc_decode_attention failed with status {rc}")
+    return out
 
 
 def compress_one(q, k, v, n_q_heads, w, c, l_max):

@@ -263,3 +263,43 @@ int orc_compress_layers(int dtype, int64_t T, int64_t t_q, int n_q_heads,
   free(sel);
   return rc;
 }
+
+/*
+ * Decode attention over one KV head's compacted cache: the step that consumes
+ * the compressed cache (the ChunkKV page's latency / throughput section times
+ * decoding over it).  Each of the G query heads of the KV head attends with
+ * one new query over the n kept rows: weights softmax(q . k_i / sqrt(d))
+ * (Kara eq. (1)), output sum_i weight_i * v_i.  Reading: the new token's own
+ * key and value are not part of the cache here (an engine appends them); an
+ * empty cache (n == 0) gives zeros.
+ * q [G][d], k and v [n][d] (one head's kept rows in order), out [G][d].
+ */
+int orc_decode_attention(int dtype, int64_t n, int G, int d, const void *q,
+                         const void *k, const void *v, double *out) {
+  if (n < 0 || G < 1 || d < 1 || (dtype != ORC_F32 && dtype != ORC_BF16))
+    return ORC_EINVAL;
+  for (int64_t e = 0; e < (int64_t)G * d; ++e) out[e] = 0.0;
+  if (n == 0) return ORC_OK;
+  double *x = (double *)malloc((size_t)n * sizeof(double));
+  if (!x) return ORC_ENOMEM;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  for (int g = 0; g < G; ++g) {
+    for (int64_t i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j)
+        acc += widen(q, dtype, (int64_t)g * d + j) * widen(k, dtype, i * d + j);
+      x[i] = acc * inv_sqrt_d;
+    }
+    double m = x[0];
+    for (int64_t i = 1; i < n; ++i)
+      if (x[i] > m) m = x[i];
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += exp(x[i] - m);
+    for (int64_t i = 0; i < n; ++i) {
+      const double p = exp(x[i] - m) / s;
+      for (int j = 0; j < d; ++j) out[(int64_t)g * d + j] += p * widen(v, dtype, i * d + j);
+    }
+  }
+  free(x);
+  return ORC_OK;
+}

@@ -351,3 +351,70 @@ def test_page_kv_bytes_per_token():
     assert abs(b / 2**20 - f["kv_bytes_per_token_7b"]["value_mb"]) < 1e-9
     tot = b * f["kv_bytes_10k_prompt_7b"]["tokens"]
     assert abs(tot / 1e9 - f["kv_bytes_10k_prompt_7b"]["value_gb"]) / 5.0 < 0.05
+
+
+# ------------------------------------------------- decode attention (consumer) --
+# The consumer of the compacted cache: one decode query per query head
+# attending over the kept rows with softmax(q . k / sqrt(d)) weights (Kara
+# eq. (1)).
+
+def test_decode_single_row_returns_its_value():
+    # n = 1: the only weight is 1, so every query head returns that value row
+    # exactly, whatever the query.
+    rng = np.random.default_rng(21)
+    q, k, v = _rand((3, 16), rng), _rand((1, 16), rng), _rand((1, 16), rng)
+    np.testing.assert_array_equal(oracle.decode_attention(q, k, v),
+                                  np.repeat(v.astype(np.float64), 3, axis=0))
+
+
+@pytest.mark.parametrize("case", ["zero_query", "equal_keys"])
+def test_decode_uniform_weights_give_the_mean(case):
+    # Closed form: a zero query, or identical keys, make every logit equal, so
+    # the output is the plain mean of the value rows.
+    rng = np.random.default_rng(22)
+    n, d = 9, 12
+    q = np.zeros((2, d), np.float32) if case == "zero_query" else _rand((2, d), rng)
+    k = _rand((n, d), rng) if case == "zero_query" else np.repeat(_rand((1, d), rng), n, axis=0)
+    v = _rand((n, d), rng)
+    np.testing.assert_allclose(oracle.decode_attention(q, k, v),
+                               np.repeat(v.astype(np.float64).mean(axis=0, keepdims=True), 2, axis=0),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_decode_two_rows_logistic_closed_form():
+    # Two rows: the weights are the logistic function of the scaled logit
+    # difference, w_1 = 1 / (1 + exp((x_2 - x_1))) with x_i = q . k_i / sqrt(d).
+    # Catches a missing 1/sqrt(d), a sign error or swapped value rows.
+    rng = np.random.default_rng(23)
+    d = 20
+    q, k, v = _rand((4, d), rng), _rand((2, d), rng) * 2, _rand((2, d), rng)
+    q64, k64, v64 = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    x = q64 @ k64.T / math.sqrt(d)
+    w1 = 1.0 / (1.0 + np.exp(x[:, 1] - x[:, 0]))
+    want = w1[:, None] * v64[0] + (1.0 - w1)[:, None] * v64[1]
+    np.testing.assert_allclose(oracle.decode_attention(q, k, v), want, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_matches_library_softmax_and_row_order_is_irrelevant():
+    # Against scipy's softmax on fp64 copies; permuting the kept rows (keys and
+    # values together) leaves the output unchanged up to rounding.
+    rng = np.random.default_rng(24)
+    n, G, d = 57, 4, 32
+    q, k, v = _rand((G, d), rng), _rand((n, d), rng) * 3, _rand((n, d), rng)
+    P = scipy.special.softmax(q.astype(np.float64) @ k.astype(np.float64).T / math.sqrt(d), axis=1)
+    out = oracle.decode_attention(q, k, v)
+    np.testing.assert_allclose(out, P @ v.astype(np.float64), rtol=1e-12, atol=1e-13)
+    perm = rng.permutation(n)
+    np.testing.assert_allclose(oracle.decode_attention(q, k[perm], v[perm]), out, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_bf16_widens_like_torch_and_empty_cache_is_zero():
+    rng = np.random.default_rng(25)
+    qt = torch.from_numpy(_rand((2, 16), rng)).to(torch.bfloat16)
+    kt = torch.from_numpy(_rand((7, 16), rng)).to(torch.bfloat16)
+    vt = torch.from_numpy(_rand((7, 16), rng)).to(torch.bfloat16)
+    a = oracle.decode_attention(kvsynth.bf16_bits(qt), kvsynth.bf16_bits(kt), kvsynth.bf16_bits(vt))
+    b = oracle.decode_attention(qt.float().numpy(), kt.float().numpy(), vt.float().numpy())
+    np.testing.assert_array_equal(a, b)
+    empty = np.zeros((0, 16), np.float32)
+    np.testing.assert_array_equal(oracle.decode_attention(_rand((2, 16), rng), empty, empty), np.zeros((2, 16)))

@@ -8,7 +8,9 @@ off-by-one chunk bounds (step 3), averaged short last chunk, causal masking,
 reversed tie order and ascending sort in TopK (step 4), a short recent window
 (step 5), gathering the wrong head (step 6), reused layers gathering the
 anchor layer's cache (Algorithm 2), a bad bf16 widening and swapped key
-strides.
+strides; in the decode-attention consumer, a dropped 1/sqrt(d), a flipped
+exponent sign, values taken from the keys and every query head reading the
+first query.
 """
 import concurrent.futures
 import os
@@ -39,6 +41,10 @@ MUTATIONS = {
     "gather_head0": ("(int64_t)head * head_stride) * elem_bytes", "(int64_t)0 * head_stride) * elem_bytes"),
     "reuse_anchor_cache": ("orc_gather(n, idx, eb, d, k[l],", "orc_gather(n, idx, eb, d, k[anchor],"),
     "bf16_shift": ("<< 16;", "<< 15;"),
+    "decode_drop_scale": ("x[i] = acc * inv_sqrt_d;", "x[i] = acc;"),
+    "decode_exp_sign": ("const double p = exp(x[i] - m) / s;", "const double p = exp(m - x[i]) / s;"),
+    "decode_values_from_keys": ("+= p * widen(v, dtype, i * d + j);", "+= p * widen(k, dtype, i * d + j);"),
+    "decode_query_head0": ("widen(q, dtype, (int64_t)g * d + j)", "widen(q, dtype, (int64_t)0 * d + j)"),
     "k_strides_swapped": ("widen(k, dtype, t * k_tok_stride + (int64_t)h * k_head_stride + i)",
                           "widen(k, dtype, t * k_head_stride + (int64_t)h * k_tok_stride + i)"),
 }
@@ -50,7 +56,7 @@ def _run(name, tmp):
     assert src.count(a) >= 1, name
     c_path = os.path.join(tmp, name + ".c")
     so_path = os.path.join(tmp, name + ".so")
-    open(c_path, "w").write(src.replace(a, b))
+    open(c_path, "w").write(src.replace(a, b, 1))   # the first occurrence: the function the mistake names
     subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-o", so_path, c_path, "-lm"])
     env = dict(os.environ, CHUNKKV_ORACLE_LIB=so_path)
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
