@@ -118,6 +118,49 @@ def copy_peak(n: int, start, stop, step_gbps: float, reps: int = 5):
             "step_hbm_frac": step_gbps / gbps}
 
 
+def decode_context(wl, cache, prob, bufs, args, start, stop):
+    """Decode attention of one new query per query head over layer 0's
+    compacted cache, against the same kernel over that layer's full cache (every
+    token kept: l_max = T), per layer."""
+    import torch
+    from kv_cache_compression_win_amd import chunkkv as ck
+    B, Hq, d = len(wl.seq_lens), wl.n_q_heads, wl.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+
+    def timed(p, k_out, v_out, lengths):
+        ws_n = ck.decode_workspace_bytes(p)
+        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            ck.decode_attention(p, q, k_out, v_out, lengths, out, ws, ws_n)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            ck.decode_attention(p, q, k_out, v_out, lengths, out, ws, ws_n)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps * 1e3
+
+    nh = B * wl.n_kv_heads
+    lens_c = bufs.lengths[:nh]
+    kept = int(lens_c.sum().item())
+    us_c = timed(prob, bufs.k_out[0], bufs.v_out[0], lens_c)
+    # the full cache of layer 0, head-major, from the library itself with every token kept
+    prob_f = ck.make_problem(ck.BF16, wl.seq_lens, wl.seq_lens, Hq, wl.n_kv_heads, d, wl.window, wl.chunk)
+    bf = ck.Buffers(prob_f, 1, 1, d, torch.bfloat16, "cuda")
+    ck.compress_layers(prob_f, 1, [cache["q_win"][0]], [cache["k"][0]], [cache["v"][0]], [bf.k_out[0]],
+                       [bf.v_out[0]], bf.scores, bf.indices, bf.lengths, bf.workspace, bf.ws_bytes)
+    us_f = timed(prob_f, bf.k_out[0], bf.v_out[0], bf.lengths[:nh])
+    full = sum(wl.seq_lens) * wl.n_kv_heads
+    return {"per_layer_us": {"compressed": us_c, "full": us_f}, "speedup": us_f / us_c,
+            "rows": {"compressed": kept, "full": full},
+            # each kept K and V row is read once
+            "hbm_gbps": {"compressed": 2 * kept * d * 2 / (us_c * 1e-6) / 1e9,
+                         "full": 2 * full * d * 2 / (us_f * 1e-6) / 1e9}}
+
+
 def hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args, start, stop):
     """The hybrid layer policy (ChunkKV page, section 5.7): the lower half of
     the layers keeps chunk size c, the upper half scores single tokens (c = 1,
@@ -381,6 +424,8 @@ def main():
             "score_ms": mean_all(0, 1), "combine_select_ms": mean_all(1, 2), "gather_ms": g_ms,
             "gather_hbm": {"achieved": g_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": g_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": g_bytes}}
+    if args.context == "on":
+        extra["decode"] = decode_context(wl, cache, prob, bufs, args, start, stop)
     if args.context == "on" and L >= 4 and wl.chunk > 1:
         extra["hybrid_policy"] = hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args,
                                                start, stop)

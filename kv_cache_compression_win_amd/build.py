@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libchunkkv.so")
-SOURCES = ["api.hip", "score_mfma.hip", "score_generic.hip", "combine.hip", "select.hip", "gather.hip"]
+SOURCES = ["api.hip", "score_mfma.hip", "score_generic.hip", "combine.hip", "select.hip", "gather.hip",
+           "decode.hip"]
 ARCH = os.environ.get("CHUNKKV_OFFLOAD_ARCH", "gfx950")
 
 

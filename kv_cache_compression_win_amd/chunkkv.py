@@ -21,7 +21,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 N_PHASE_EVENTS = 4
 
 SYMBOLS = ("chunkkv_plan", "chunkkv_workspace_bytes", "chunkkv_score", "chunkkv_select",
-           "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_last_error")
+           "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_decode_workspace_bytes",
+           "chunkkv_decode_attention", "chunkkv_last_error")
 
 
 class ChunkKVError(RuntimeError):
@@ -79,6 +80,10 @@ def lib() -> ctypes.CDLL:
         L.chunkkv_compress_layers.restype = ctypes.c_int
         L.chunkkv_compress_layers.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                               vp, vp]
+        L.chunkkv_decode_workspace_bytes.restype = sz
+        L.chunkkv_decode_workspace_bytes.argtypes = [P]
+        L.chunkkv_decode_attention.restype = ctypes.c_int
+        L.chunkkv_decode_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.chunkkv_last_error.restype = ctypes.c_char_p
         L.chunkkv_last_error.argtypes = []
         _lib = L
@@ -224,6 +229,21 @@ def select(prob, scores, indices, lengths, stream=None) -> None:
 def gather(prob, k, v, indices, lengths, k_out, v_out, stream=None) -> None:
     _check(lib().chunkkv_gather(prob.ref, _ptr(k), _ptr(v), _ptr(indices), _ptr(lengths),
                                 _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def decode_workspace_bytes(prob: ProblemHandle) -> int:
+    n = lib().chunkkv_decode_workspace_bytes(prob.ref)
+    if n == 0:
+        raise ChunkKVError(ERR_INVALID_ARG, last_error() or "invalid problem")
+    return n
+
+
+def decode_attention(prob, q_dec, k_out, v_out, lengths, out, workspace, workspace_nbytes: int,
+                     stream=None) -> None:
+    """chunkkv_decode_attention: one decode query per query head over the
+    compacted cache (out fp32 [n_seqs][n_q_heads][head_dim])."""
+    _check(lib().chunkkv_decode_attention(prob.ref, _ptr(q_dec), _ptr(k_out), _ptr(v_out), _ptr(lengths),
+                                          _ptr(out), _ptr(workspace), workspace_nbytes, _stream(stream)))
 
 
 def compress_layers(prob, n_reuse: int, q_win: Sequence, k: Sequence, v: Sequence, k_out: Sequence,

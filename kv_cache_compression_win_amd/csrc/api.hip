@@ -17,6 +17,7 @@
 
 #include "chunkkv.h"
 #include "chunkkv_internal.h"
+#include "decode_internal.h"
 
 namespace {
 
@@ -565,6 +566,69 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
   if (!gather_events && (e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+  return ok();
+}
+
+size_t chunkkv_decode_workspace_bytes(const chunkkv_problem* p) {
+  Plan pl;
+  if (make_plan(p, pl)) return 0;
+  int64_t blocks = 0;
+  for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + kDecRows - 1) / kDecRows);
+  return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + 2) * sizeof(float));
+}
+
+int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const void* k_out, const void* v_out,
+                             const int32_t* lengths, float* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Plan pl;
+  const int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!q_dec || !k_out || !v_out || !lengths || !out)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "q_dec, k_out, v_out, lengths and out must be non-NULL");
+  if (!aligned16(k_out) || !aligned16(v_out) || reinterpret_cast<uintptr_t>(q_dec) % pl.eb ||
+      reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "k_out and v_out must be 16-byte aligned");
+  const size_t need = chunkkv_decode_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(CHUNKKV_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0,
+                need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t part0 = 0;
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    DecodeParams P{};
+    P.q = q_dec;
+    P.k = k_out;
+    P.v = v_out;
+    P.lengths = lengths;
+    P.out = out;
+    P.part = static_cast<float*>(workspace);
+    P.n_seqs = nb;
+    P.H_q = pl.Hq;
+    P.H_kv = pl.Hkv;
+    P.G = pl.G;
+    P.d = pl.d;
+    P.row_bytes = pl.d * pl.eb;
+    P.elem_bytes = pl.eb;
+    P.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(pl.d)));
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.qseq[i] = b0 + i;
+      P.item0[i] = items;
+      P.blocks_per_head[i] = (sq.L_cap + kDecRows - 1) / kDecRows;
+      P.L_cap[i] = sq.L_cap;
+      P.len_off[i] = (b0 + i) * pl.Hkv;
+      P.index_off[i] = sq.index_off;
+      P.part_off[i] = part0;
+      part0 += static_cast<int64_t>(pl.Hkv) * P.blocks_per_head[i];
+      items += pl.Hkv * P.blocks_per_head[i];
+    }
+    P.item0[nb] = items;
+    if (decode_lds_bytes(P) > 160 * 1024) return fail(CHUNKKV_ERR_UNSUPPORTED, "head_dim too large for decode");
+    const hipError_t e = launch_decode(P, items, nb * pl.Hq, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
   return ok();
 }
 

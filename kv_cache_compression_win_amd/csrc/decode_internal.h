@@ -1,0 +1,36 @@
+// Internal definitions of the decode-attention kernels (not part of the C-ABI).
+#pragma once
+
+#include "chunkkv_internal.h"
+
+namespace ckv {
+
+constexpr int kDecRows = kThreads;   // kept rows per decode work item (one per thread for the logits)
+constexpr int kDecQ = 8;             // query heads of a group handled per pass
+
+// Work item = (sequence b, KV head h, block of kDecRows kept rows).  Partials
+// part[((part_off[b] + h*blocks_per_head[b] + blk)*G + g)*(d + 2) + ...] =
+// (block max, block sum of exponentials, d unnormalised value sums).
+struct DecodeParams {
+  const void* q;                // [n_seqs][H_q][d], element type of the cache
+  const void* k;                // compacted caches, rows of row_bytes
+  const void* v;
+  const int32_t* lengths;       // [n_seqs * H_kv]
+  float* out;                   // [n_seqs][H_q][d]
+  float* part;
+  int32_t n_seqs, H_q, H_kv, G, d, row_bytes, elem_bytes;
+  float inv_sqrt_d;
+  int32_t qseq[kMaxSeqs];       // global sequence index of launch sequence b
+  int32_t item0[kMaxSeqs + 1];
+  int32_t blocks_per_head[kMaxSeqs];
+  int32_t L_cap[kMaxSeqs];
+  int32_t len_off[kMaxSeqs];    // b_global * H_kv
+  int64_t index_off[kMaxSeqs];
+  int64_t part_off[kMaxSeqs];
+};
+
+size_t decode_lds_bytes(const DecodeParams& p);
+// Partial blocks (n_items) then the merge (one workgroup per output query head).
+hipError_t launch_decode(const DecodeParams& p, int n_items, int n_heads_out, hipStream_t s);
+
+}  // namespace ckv
