@@ -223,7 +223,7 @@ int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t 
 /* Message of this thread's last non-OK status ("" if none). */
 /*
  * Workspace needed by chunkkv_decode_attention for problem p: per-block
- * partials of every (sequence, KV head, block of 256 kept rows, query head).
+ * partials of every (sequence, KV head, block of 64 kept rows, query head).
  * Host only.  Returns 0 on invalid input.
  */
 size_t chunkkv_decode_workspace_bytes(const chunkkv_problem *p);

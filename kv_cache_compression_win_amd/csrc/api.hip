@@ -303,6 +303,18 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
   return hipSuccess;
 }
 
+// Kept rows per decode work item: a multiple of kDecRows giving about
+// kDecodeBlocks work items over the whole problem (the blocks' partials are
+// merged per query head), so short caches still spread over the GPU and long
+// ones keep the merge short.
+constexpr int64_t kDecodeBlocks = 512;
+int decode_rows_per_block(const Plan& pl) {
+  int64_t rows = 0;
+  for (const Seq& sq : pl.seq) rows += static_cast<int64_t>(pl.Hkv) * sq.L_cap;
+  const int64_t per = std::max<int64_t>((rows + kDecodeBlocks - 1) / kDecodeBlocks, kDecRows);
+  return static_cast<int>(std::min<int64_t>(round_up(per, kDecRows), int64_t{1} << 30));
+}
+
 // Scores of nl scoring layers: chunk partials then the log-sum-exp combine,
 // or (pl.two_pass) statistics, row statistics and a final pass over the keys.
 hipError_t run_scores(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U, float2* st,
@@ -572,8 +584,9 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
 size_t chunkkv_decode_workspace_bytes(const chunkkv_problem* p) {
   Plan pl;
   if (make_plan(p, pl)) return 0;
+  const int rpb = decode_rows_per_block(pl);
   int64_t blocks = 0;
-  for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + kDecRows - 1) / kDecRows);
+  for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + rpb - 1) / rpb);
   return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + 2) * sizeof(float));
 }
 
@@ -593,6 +606,7 @@ int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const 
     return fail(CHUNKKV_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0,
                 need);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rpb = decode_rows_per_block(pl);
   int64_t part0 = 0;
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
@@ -616,7 +630,8 @@ int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const 
       const Seq& sq = pl.seq[b0 + i];
       P.qseq[i] = b0 + i;
       P.item0[i] = items;
-      P.blocks_per_head[i] = (sq.L_cap + kDecRows - 1) / kDecRows;
+      P.blocks_per_head[i] = (sq.L_cap + rpb - 1) / rpb;
+      P.rows_per_block[i] = rpb;
       P.L_cap[i] = sq.L_cap;
       P.len_off[i] = (b0 + i) * pl.Hkv;
       P.index_off[i] = sq.index_off;

@@ -5,12 +5,14 @@
 // eq. (1)); the output is the weighted sum of the kept value rows.
 //
 // Split over the rows (flash-decoding style): work item = (sequence, KV head,
-// block of kDecRows rows).  An item computes, for up to kDecQ query heads of
-// the group at a time, every row's logit (one row per thread, the queries in
-// LDS), the block's maximum and sum of exponentials, and the unnormalised
-// value sum (consecutive threads read consecutive 16-byte pieces of a value
-// row; per-thread partial sums are added over the row subsets through LDS in
-// a fixed order).  A second kernel merges the blocks of each query head by
+// block of rows), walked kDecRows rows at a time with a running maximum and
+// sum of exponentials (the value sums rescaled when the maximum grows).  Per
+// step, for up to kDecQ query heads of the group at a time: every row's logit
+// (a team of threads per key row, partial dot products added by a butterfly
+// inside the team; the queries in LDS), the step's weights (one lane per row),
+// and the value sums (consecutive threads read consecutive 16-byte pieces of
+// a value row; per-thread partial sums are added over the row subsets through
+// LDS in a fixed order at the end).  A second kernel merges the blocks of each query head by
 // their (max, sum) and normalises.  Everything is accumulated in fp32 in a
 // fixed order: results are deterministic.
 #include "decode_internal.h"
@@ -42,10 +44,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
   const int tid = threadIdx.x;
   const int d = P.d, pieces = P.row_bytes >> 4;
   float* q_l = smem;                             // [kDecQ][d]
-  float* p_l = q_l + kDecQ * d;                  // [kDecRows][kDecQ] weights
+  float* p_l = q_l + kDecQ * d;                  // [kDecRows][kDecQ] logits, then weights
   float* acc_l = p_l + kDecRows * kDecQ;         // [subsets][kDecQ][d] partial value sums
   __shared__ float red[kThreads / 64][kDecQ];
-  __shared__ float mx_l[kDecQ], sum_l[kDecQ];
+  __shared__ float res[kDecQ];
 
   int item = blockIdx.x;
   int b = 0;
@@ -54,14 +56,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
   const int nblk = P.blocks_per_head[b];
   const int h = item / nblk, blk = item - h * nblk;
   const int n = min(max(P.lengths[P.len_off[b] + h], 0), P.L_cap[b]);
-  const int r0 = blk * kDecRows;
-  if (r0 >= n) return;                           // the merge reads only blocks below n
-  const int rows = min(kDecRows, n - r0);
-  const int64_t row0 = P.index_off[b] + static_cast<int64_t>(h) * P.L_cap[b] + r0;
-  const char* kb = static_cast<const char*>(P.k) + row0 * P.row_bytes;
-  const char* vb = static_cast<const char*>(P.v) + row0 * P.row_bytes;
+  const int rpb = P.rows_per_block[b];
+  const int r_begin = blk * rpb;
+  if (r_begin >= n) return;                      // the merge reads only blocks below n
+  const int r_end = min(n, r_begin + rpb);
+  const int64_t head0 = P.index_off[b] + static_cast<int64_t>(h) * P.L_cap[b];
   const int subsets = kThreads / pieces;         // value-phase row subsets
-  const int lane = tid & 63, wave = tid >> 6;
+  const int pc_v = tid % pieces, sub = tid / pieces;
 
   for (int g0 = 0; g0 < P.G; g0 += kDecQ) {
     const int nq = min(kDecQ, P.G - g0);
@@ -74,82 +75,138 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                                : __uint_as_float(static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(qp)) << 16);
     }
     __syncthreads();
-    // logits: one row per thread, pieces in order
-    float x[kDecQ];
+    // running maximum and sum of exponentials of the block's rows so far, and
+    // this thread's unnormalised value sums (rescaled when the maximum grows)
+    float m_run[kDecQ], l_run[kDecQ], a[kDecQ][EPP];
 #pragma unroll
-    for (int g = 0; g < kDecQ; ++g) x[g] = 0.0f;
-    const bool live = tid < rows;
-    if (live) {
-      const u32x4* kr = reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(tid) * P.row_bytes);
-      for (int pc = 0; pc < pieces; ++pc) {
-        float f[EPP];
-        widen16<EB>(kr[pc], f);
+    for (int g = 0; g < kDecQ; ++g) {
+      m_run[g] = -INFINITY;
+      l_run[g] = 0.0f;
 #pragma unroll
-        for (int g = 0; g < kDecQ; ++g) {
-          if (g < nq) {
-            const float* qg = q_l + g * d + pc * EPP;
+      for (int e = 0; e < EPP; ++e) a[g][e] = 0.0f;
+    }
+    // logits: a team of TS threads per key row (TS = 4, 2 or 1 dividing the
+    // piece count), each thread a run of consecutive 16-byte pieces, partial
+    // dot products added by a butterfly inside the team
+    const int TS = (pieces % 4 == 0) ? 4 : ((pieces % 2 == 0) ? 2 : 1);
+    const int ppt = pieces / TS, tp = tid % TS;
+    for (int c0 = r_begin; c0 < r_end; c0 += kDecRows) {
+      const int rows = min(kDecRows, r_end - c0);
+      const char* kb = static_cast<const char*>(P.k) + (head0 + c0) * P.row_bytes;
+      const char* vb = static_cast<const char*>(P.v) + (head0 + c0) * P.row_bytes;
+      // this step's value pieces are loaded first: they do not depend on the
+      // weights, so their latency overlaps the logits
+      constexpr int kVMax = 4;   // rows per subset held in registers; more rows are read in the value phase
+      u32x4 vr[kVMax];
+      if (sub < subsets) {
 #pragma unroll
-            for (int e = 0; e < EPP; ++e) x[g] = fmaf(f[e], qg[e], x[g]);
+        for (int t = 0; t < kVMax; ++t) {
+          const int i = sub + t * subsets;
+          if (i < rows) vr[t] = reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc_v];
+        }
+      }
+      for (int r = tid / TS; r < rows; r += kThreads / TS) {
+        const u32x4* kr = reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(r) * P.row_bytes);
+        float x[kDecQ];
+#pragma unroll
+        for (int g = 0; g < kDecQ; ++g) x[g] = 0.0f;
+        for (int k = 0; k < ppt; ++k) {
+          const int pc = tp * ppt + k;
+          float f[EPP];
+          widen16<EB>(kr[pc], f);
+#pragma unroll
+          for (int g = 0; g < kDecQ; ++g) {
+            if (g < nq) {
+              const float* qg = q_l + g * d + pc * EPP;
+#pragma unroll
+              for (int e = 0; e < EPP; ++e) x[g] = fmaf(f[e], qg[e], x[g]);
+            }
+          }
+        }
+        for (int o = TS >> 1; o > 0; o >>= 1)
+#pragma unroll
+          for (int g = 0; g < kDecQ; ++g) x[g] += __shfl_xor(x[g], o, 64);
+        if (tp == 0)
+#pragma unroll
+          for (int g = 0; g < kDecQ; ++g) p_l[r * kDecQ + g] = x[g] * P.inv_sqrt_d;
+      }
+      __syncthreads();
+      // each wave takes query heads wave, wave + 4 (one lane per row of the
+      // step): the step's maximum, the new running maximum, the weights and
+      // their sum, published through LDS
+      {
+        const int lane = tid & 63, wave = tid >> 6;
+        const bool live = lane < rows;
+#pragma unroll
+        for (int gg = 0; gg < kDecQ / (kThreads / 64); ++gg) {
+          const int g = wave + gg * (kThreads / 64);
+          const float x = (live && g < nq) ? p_l[lane * kDecQ + g] : -INFINITY;
+          float m = x;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          float mr = m_run[0];   // m_run[g] without indexing the register array by a lane-varying value
+#pragma unroll
+          for (int gi = 1; gi < kDecQ; ++gi) mr = gi == g ? m_run[gi] : mr;
+          const float mn = fmaxf(mr, m);
+          const float pw = (live && g < nq) ? expf(x - mn) : 0.0f;
+          p_l[lane * kDecQ + g] = pw;
+          float sc = pw;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) sc += __shfl_xor(sc, o, 64);
+          if (lane == 0) {
+            res[g] = mn;
+            red[0][g] = sc;
           }
         }
       }
-    }
-    // block maximum, exponentials and their sum per query head
+      __syncthreads();
+      float f[kDecQ];
 #pragma unroll
-    for (int g = 0; g < kDecQ; ++g) {
-      float m = (live && g < nq) ? x[g] * P.inv_sqrt_d : -INFINITY;
-      x[g] = m;
+      for (int g = 0; g < kDecQ; ++g) {
+        const float mn = res[g];
+        f[g] = m_run[g] == -INFINITY ? 0.0f : expf(m_run[g] - mn);
+        l_run[g] = l_run[g] * f[g] + red[0][g];
+        m_run[g] = mn;
+      }
+      // value sums: thread (subset, piece) adds rows subset, subset + subsets, ...
+      if (sub < subsets) {
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      if (lane == 0) red[wave][g] = m;
-    }
-    __syncthreads();
-    if (tid < kDecQ) {
-      float m = red[0][tid];
-      for (int w2 = 1; w2 < kThreads / 64; ++w2) m = fmaxf(m, red[w2][tid]);
-      mx_l[tid] = m;
-    }
-    __syncthreads();
+        for (int g = 0; g < kDecQ; ++g)
 #pragma unroll
-    for (int g = 0; g < kDecQ; ++g) {
-      const float p = (live && g < nq) ? expf(x[g] - mx_l[g]) : 0.0f;
-      if (tid < kDecRows) p_l[tid * kDecQ + g] = p;
-      float s = p;
+          for (int e = 0; e < EPP; ++e) a[g][e] *= f[g];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-      if (lane == 0) red[wave][g] = s;
-    }
-    __syncthreads();
-    if (tid < kDecQ) {
-      float s = red[0][tid];
-      for (int w2 = 1; w2 < kThreads / 64; ++w2) s += red[w2][tid];
-      sum_l[tid] = s;
-    }
-    // unnormalised value sums: thread (subset, piece) adds rows subset,
-    // subset + subsets, ... of its piece
-    const int pc = tid % pieces, sub = tid / pieces;
-    float a[kDecQ][EPP];
+        for (int t = 0; t < kVMax; ++t) {
+          const int i = sub + t * subsets;
+          if (i < rows) {
+            float fv[EPP];
+            widen16<EB>(vr[t], fv);
 #pragma unroll
-    for (int g = 0; g < kDecQ; ++g)
+            for (int g = 0; g < kDecQ; ++g) {
+              const float p = p_l[i * kDecQ + g];
 #pragma unroll
-      for (int e = 0; e < EPP; ++e) a[g][e] = 0.0f;
-    if (sub < subsets) {
-      for (int i = sub; i < rows; i += subsets) {
-        float f[EPP];
-        widen16<EB>(reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc], f);
+              for (int e = 0; e < EPP; ++e) a[g][e] = fmaf(p, fv[e], a[g][e]);
+            }
+          }
+        }
+        for (int i = sub + kVMax * subsets; i < rows; i += subsets) {   // wide rows: fewer subsets
+          float fv[EPP];
+          widen16<EB>(reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc_v], fv);
 #pragma unroll
-        for (int g = 0; g < kDecQ; ++g) {
-          const float p = p_l[i * kDecQ + g];
+          for (int g = 0; g < kDecQ; ++g) {
+            const float p = p_l[i * kDecQ + g];
 #pragma unroll
-          for (int e = 0; e < EPP; ++e) a[g][e] = fmaf(p, f[e], a[g][e]);
+            for (int e = 0; e < EPP; ++e) a[g][e] = fmaf(p, fv[e], a[g][e]);
+          }
         }
       }
+      __syncthreads();   // p_l, res and red are rewritten by the next chunk
+    }
+    if (sub < subsets)
 #pragma unroll
       for (int g = 0; g < kDecQ; ++g)
         if (g < nq)
 #pragma unroll
-          for (int e = 0; e < EPP; ++e) acc_l[(sub * kDecQ + g) * d + pc * EPP + e] = a[g][e];
-    }
+          for (int e = 0; e < EPP; ++e) acc_l[(sub * kDecQ + g) * d + pc_v * EPP + e] = a[g][e];
     __syncthreads();
     // the block's partial for each query head of the pass: (max, sum, value sums)
     float* part = P.part + ((P.part_off[b] + static_cast<int64_t>(h) * nblk + blk) * P.G + g0) * (d + 2);
@@ -160,34 +217,93 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
       part[g * (d + 2) + 2 + j] = s;
     }
     if (tid < nq) {
-      part[tid * (d + 2)] = mx_l[tid];
-      part[tid * (d + 2) + 1] = sum_l[tid];
+      part[tid * (d + 2)] = m_run[tid];
+      part[tid * (d + 2) + 1] = l_run[tid];
     }
     __syncthreads();   // before the next pass rewrites q_l, p_l and acc_l
   }
 }
 
-// out[b][hq][:] = sum_blocks e^(m_blk - M) o_blk / sum_blocks e^(m_blk - M) l_blk,
-// blocks merged in order; zeros when the head keeps no rows.
+// out[b][hq][:] = sum_blocks e^(m_blk - M) o_blk / sum_blocks e^(m_blk - M) l_blk
+// over the blocks that hold rows; zeros when the head keeps no rows.  One
+// workgroup per query head: the blocks' weights are formed in parallel (into
+// LDS), then thread (subset, j) adds blocks subset, subset + S, ... of output
+// element j and the S subsets are added in order.
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeParams P) {
-  int item = blockIdx.x;   // (sequence, query head)
+  extern __shared__ float w_l[];   // [blocks_per_head] weights, then [S][d] subset sums
+  __shared__ float red[kThreads / 64];
+  __shared__ float bc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int item = blockIdx.x;     // (sequence, query head)
   const int b = item / P.H_q, hq = item - b * P.H_q;
   const int h = hq / P.G, g = hq - h * P.G;
   const int d = P.d;
   const int n = min(max(P.lengths[P.len_off[b] + h], 0), P.L_cap[b]);
-  const int nb = (n + kDecRows - 1) / kDecRows;
+  const int nb = (n + P.rows_per_block[b] - 1) / P.rows_per_block[b];
+  float* o = P.out + (static_cast<int64_t>(P.qseq[b]) * P.H_q + hq) * d;
+  if (nb == 0) {
+    for (int j = tid; j < d; j += kThreads) o[j] = 0.0f;
+    return;
+  }
   const float* part = P.part + (P.part_off[b] + static_cast<int64_t>(h) * P.blocks_per_head[b]) * P.G * (d + 2) +
                       static_cast<int64_t>(g) * (d + 2);
   const int64_t stride = static_cast<int64_t>(P.G) * (d + 2);
-  float M = -INFINITY;
-  for (int k = 0; k < nb; ++k) M = fmaxf(M, part[k * stride]);
-  float L = 0.0f;
-  for (int k = 0; k < nb; ++k) L += expf(part[k * stride] - M) * part[k * stride + 1];
-  float* o = P.out + (static_cast<int64_t>(P.qseq[b]) * P.H_q + hq) * d;
-  for (int j = threadIdx.x; j < d; j += kThreads) {
+  // M: the largest block maximum
+  float m = -INFINITY;
+  for (int k = tid; k < nb; k += kThreads) m = fmaxf(m, part[k * stride]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float x = red[0];
+    for (int w2 = 1; w2 < kThreads / 64; ++w2) x = fmaxf(x, red[w2]);
+    bc = x;
+  }
+  __syncthreads();
+  const float M = bc;
+  // block weights e^(m_blk - M) and L = sum_blocks weight * l_blk
+  float l = 0.0f;
+  for (int k = tid; k < nb; k += kThreads) {
+    const float wk = expf(part[k * stride] - M);
+    w_l[k] = wk;
+    l += wk * part[k * stride + 1];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
+  __syncthreads();
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  if (tid == 0) {
+    float x = red[0];
+    for (int w2 = 1; w2 < kThreads / 64; ++w2) x += red[w2];
+    bc = x;
+  }
+  __syncthreads();
+  const float L = bc;
+  // output elements: S = kThreads / d subsets of blocks per element
+  const int S = max(1, kThreads / d);
+  float* sub_l = w_l + P.blocks_per_head[b];
+  for (int e = tid; e < S * d; e += kThreads) {
+    const int sub = e / d, j = e - sub * d;
     float s = 0.0f;
-    for (int k = 0; k < nb; ++k) s += expf(part[k * stride] - M) * part[k * stride + 2 + j];
-    o[j] = nb > 0 ? s / L : 0.0f;
+    int k = sub;
+    for (; k + 3 * S < nb; k += 4 * S) {   // four independent loads in flight
+      const float a0 = part[k * stride + 2 + j], a1 = part[(k + S) * stride + 2 + j];
+      const float a2 = part[(k + 2 * S) * stride + 2 + j], a3 = part[(k + 3 * S) * stride + 2 + j];
+      s = fmaf(w_l[k], a0, s);
+      s = fmaf(w_l[k + S], a1, s);
+      s = fmaf(w_l[k + 2 * S], a2, s);
+      s = fmaf(w_l[k + 3 * S], a3, s);
+    }
+    for (; k < nb; k += S) s = fmaf(w_l[k], part[k * stride + 2 + j], s);
+    sub_l[sub * d + j] = s;
+  }
+  __syncthreads();
+  for (int j = tid; j < d; j += kThreads) {
+    float s = 0.0f;
+    for (int sub = 0; sub < S; ++sub) s += sub_l[sub * d + j];
+    o[j] = s / L;
   }
 }
 
@@ -205,7 +321,11 @@ hipError_t launch_decode(const DecodeParams& p, int n_items, int n_heads_out, hi
                      ? launch1(decode_partial_kernel<4>, dim3(n_items), dim3(kThreads), lds, s, p)
                      : launch1(decode_partial_kernel<2>, dim3(n_items), dim3(kThreads), lds, s, p);
   if (e != hipSuccess) return e;
-  return launch1(decode_merge_kernel, dim3(n_heads_out), dim3(kThreads), 0, s, p);
+  int nbh = 1;
+  for (int i = 0; i < p.n_seqs; ++i) nbh = nbh > p.blocks_per_head[i] ? nbh : p.blocks_per_head[i];
+  const int S = kThreads / p.d > 1 ? kThreads / p.d : 1;
+  const size_t merge_lds = (static_cast<size_t>(nbh) + static_cast<size_t>(S) * p.d) * sizeof(float);
+  return launch1(decode_merge_kernel, dim3(n_heads_out), dim3(kThreads), merge_lds, s, p);
 }
 
 }  // namespace ckv

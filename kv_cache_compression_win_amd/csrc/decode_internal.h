@@ -5,10 +5,11 @@
 
 namespace ckv {
 
-constexpr int kDecRows = kThreads;   // kept rows per decode work item (one per thread for the logits)
+constexpr int kDecRows = 64;         // kept rows per step of a decode work item
 constexpr int kDecQ = 8;             // query heads of a group handled per pass
 
-// Work item = (sequence b, KV head h, block of kDecRows kept rows).  Partials
+// Work item = (sequence b, KV head h, block of rows_per_block[b] kept rows, a
+// multiple of kDecRows handled kDecRows at a time).  Partials
 // part[((part_off[b] + h*blocks_per_head[b] + blk)*G + g)*(d + 2) + ...] =
 // (block max, block sum of exponentials, d unnormalised value sums).
 struct DecodeParams {
@@ -23,6 +24,7 @@ struct DecodeParams {
   int32_t qseq[kMaxSeqs];       // global sequence index of launch sequence b
   int32_t item0[kMaxSeqs + 1];
   int32_t blocks_per_head[kMaxSeqs];
+  int32_t rows_per_block[kMaxSeqs];
   int32_t L_cap[kMaxSeqs];
   int32_t len_off[kMaxSeqs];    // b_global * H_kv
   int64_t index_off[kMaxSeqs];
