@@ -137,6 +137,20 @@ def gather(src: np.ndarray, idx: np.ndarray, head: int) -> np.ndarray:
     return dst
 
 
+def to_pages(rows: np.ndarray, table: np.ndarray, page_rows: int, pool: np.ndarray) -> None:
+    """Write one head's kept rows ``rows[n, d]`` into the page pool
+    ``pool[n_pages, page_rows, d]`` in place: the cache as fixed-size blocks of
+    consecutive KV rows, as PagedAttention keeps it (Kara page, section 2).
+    Row i goes to row ``i % page_rows`` of page ``table[i // page_rows]``; a
+    page id outside ``[0, n_pages)`` leaves its rows unwritten.  Plain loop
+    over the rows: small cases only."""
+    n_pages = pool.shape[0]
+    for i in range(rows.shape[0]):
+        page = int(table[i // page_rows])
+        if 0 <= page < n_pages:
+            pool[page, i % page_rows] = rows[i]
+
+
 def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     """Decode attention of the G queries ``q[G, d]`` over one head's kept rows
     ``k[n, d]``, ``v[n, d]`` (softmax(q . k / sqrt(d)) weights, Kara eq. (1)),

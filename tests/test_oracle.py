@@ -418,3 +418,48 @@ def test_decode_bf16_widens_like_torch_and_empty_cache_is_zero():
     np.testing.assert_array_equal(a, b)
     empty = np.zeros((0, 16), np.float32)
     np.testing.assert_array_equal(oracle.decode_attention(_rand((2, 16), rng), empty, empty), np.zeros((2, 16)))
+
+
+# ------------------------------------------------------------- paged output --
+def test_to_pages_worked_example():
+    # five rows into pages of two, table [2, 0, 1]: written out by hand
+    rows = np.repeat(np.arange(5, dtype=np.float32)[:, None], 2, axis=1)
+    pool = np.full((4, 2, 2), -1.0, dtype=np.float32)
+    oracle.to_pages(rows, np.array([2, 0, 1], dtype=np.int32), 2, pool)
+    want = np.array([[[2, 2], [3, 3]],
+                     [[4, 4], [-1, -1]],
+                     [[0, 0], [1, 1]],
+                     [[-1, -1], [-1, -1]]], dtype=np.float32)
+    assert np.array_equal(pool, want)
+
+
+def test_to_pages_one_large_page_is_the_contiguous_layout():
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, 2**16, size=(37, 8)).astype(np.uint16)
+    pool = np.zeros((1, 40, 8), dtype=np.uint16)
+    oracle.to_pages(rows, np.array([0], dtype=np.int32), 40, pool)
+    assert np.array_equal(pool[0, :37], rows) and not pool[0, 37:].any()
+
+
+@pytest.mark.parametrize("n,page_rows", [(0, 16), (1, 16), (16, 16), (97, 16), (250, 7)])
+def test_to_pages_read_back_through_the_table(n, page_rows):
+    # reading the listed pages in table order and dropping the tail gives the
+    # rows back; pages the table does not list stay as they were
+    rng = np.random.default_rng(n + page_rows)
+    rows = rng.standard_normal((n, 4)).astype(np.float32)
+    n_tab = max(1, -(-n // page_rows))
+    n_pages = n_tab + 5
+    table = rng.permutation(n_pages)[:n_tab].astype(np.int32)
+    pool = np.full((n_pages, page_rows, 4), np.nan, dtype=np.float32)
+    oracle.to_pages(rows, table, page_rows, pool)
+    back = pool[table].reshape(-1, 4)[:n]
+    assert np.array_equal(back, rows)
+    unlisted = np.setdiff1d(np.arange(n_pages), table[: -(-n // page_rows)] if n else [])
+    assert np.all(np.isnan(pool[unlisted]))
+
+
+def test_to_pages_skips_out_of_range_page_ids():
+    rows = np.arange(12, dtype=np.float64).reshape(6, 2)
+    pool = np.zeros((2, 2, 2))
+    oracle.to_pages(rows, np.array([1, -1, 2], dtype=np.int32), 2, pool)
+    assert np.array_equal(pool[1], rows[:2]) and not pool[0].any()
