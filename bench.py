@@ -161,6 +161,45 @@ def decode_context(wl, cache, prob, bufs, args, start, stop):
                          "full": 2 * full * d * 2 / (us_f * 1e-6) / 1e9}}
 
 
+def paged_context(wl, cache, prob, bufs, args, start, stop, page_rows=256):
+    """Layer 0's compaction written into pool pages of page_rows rows through a
+    shuffled block table (the PagedAttention block layout, Kara page,
+    section 2), against the contiguous gather of the same layer."""
+    import torch
+    from kv_cache_compression_win_amd import chunkkv as ck
+    from kv_cache_compression_win_amd import accounting
+    pl = ck.plan(prob)
+    d, nh = wl.head_dim, len(wl.seq_lens) * wl.n_kv_heads
+    idx, lens = bufs.indices[:pl["index_elems"]], bufs.lengths[:nh]
+    max_pages = max(-(-int(x) // page_rows) for x in pl["l_cap"])
+    n_pages = nh * max_pages
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    table = torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)
+    kp = torch.empty((n_pages, page_rows, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    ko, vo = bufs.k_out[0], bufs.v_out[0]
+    k0, v0 = cache["k"][0], cache["v"][0]
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps * 1e3
+
+    us_p = timed(lambda: ck.gather_paged(prob, k0, v0, idx, lens, table, max_pages, page_rows, n_pages, kp, vp))
+    us_c = timed(lambda: ck.gather(prob, k0, v0, idx, lens, ko, vo))
+    kept = int(lens.sum().item())
+    nbytes = accounting.gather_bytes(kept, d, 2)
+    return {"page_rows": page_rows, "n_pages": n_pages, "per_layer_us": {"paged": us_p, "contiguous": us_c},
+            "hbm_gbps": {"paged": nbytes / (us_p * 1e-6) / 1e9, "contiguous": nbytes / (us_c * 1e-6) / 1e9}}
+
+
 def hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args, start, stop):
     """The hybrid layer policy (ChunkKV page, section 5.7): the lower half of
     the layers keeps chunk size c, the upper half scores single tokens (c = 1,
@@ -426,6 +465,7 @@ def main():
                            "frac": g_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": g_bytes}}
     if args.context == "on":
         extra["decode"] = decode_context(wl, cache, prob, bufs, args, start, stop)
+        extra["paged_output"] = paged_context(wl, cache, prob, bufs, args, start, stop)
     if args.context == "on" and L >= 4 and wl.chunk > 1:
         extra["hybrid_policy"] = hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args,
                                                start, stop)

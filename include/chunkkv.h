@@ -220,7 +220,6 @@ int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t 
                             float *scores, int32_t *indices, int32_t *lengths, void *workspace,
                             size_t workspace_bytes, void *stream, void *const *phase_events);
 
-/* Message of this thread's last non-OK status ("" if none). */
 /*
  * Workspace needed by chunkkv_decode_attention for problem p: per-block
  * partials of every (sequence, KV head, block of 64 kept rows, query head).
@@ -249,6 +248,32 @@ int chunkkv_decode_attention(const chunkkv_problem *p, const void *q_dec, const 
                              const void *v_out, const int32_t *lengths, float *out,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Paged output: the same copy as chunkkv_gather (ChunkKV page, section 4.1,
+ * Algorithm 1 step 6), written into a pool of fixed-size pages of
+ * consecutive KV rows, the block layout of PagedAttention (Kara page,
+ * section 2), instead of one contiguous run per head.  Kept row i of
+ * (sequence b, KV head h) goes to row i % page_rows of page
+ * block_table[(b * n_kv_heads + h) * max_pages + i / page_rows].
+ *   k, v          DEVICE inputs (layout in chunkkv_problem)
+ *   indices, lengths  DEVICE, as written by chunkkv_select (clamped as in
+ *                 chunkkv_gather)
+ *   block_table   DEVICE int32 [n_seqs * n_kv_heads][max_pages]: the pool
+ *                 pages of each (sequence, head) in order; max_pages must
+ *                 cover ceil(L_cap_b / page_rows) for every sequence
+ *   k_pages, v_pages  DEVICE out [n_pages][page_rows][head_dim], 16-byte
+ *                 aligned; only the rows of kept rows are written.  A page id
+ *                 outside [0, n_pages) leaves its rows unwritten; pages
+ *                 listed twice get the rows of whichever copy lands last.
+ * Errors: INVALID_ARG (incl. page_rows, max_pages or n_pages < 1, a table
+ * too short for L_cap), UNSUPPORTED, HIP.
+ */
+int chunkkv_gather_paged(const chunkkv_problem *p, const void *k, const void *v,
+                         const int32_t *indices, const int32_t *lengths,
+                         const int32_t *block_table, int32_t max_pages, int32_t page_rows,
+                         int64_t n_pages, void *k_pages, void *v_pages, void *stream);
+
+/* Message of this thread's last non-OK status ("" if none). */
 const char *chunkkv_last_error(void);
 
 #ifdef __cplusplus

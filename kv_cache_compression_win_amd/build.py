@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libchunkkv.so")
 SOURCES = ["api.hip", "score_mfma.hip", "score_generic.hip", "combine.hip", "select.hip", "gather.hip",
-           "decode.hip"]
+           "decode.hip", "paged.hip"]
 ARCH = os.environ.get("CHUNKKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -22,7 +22,7 @@ N_PHASE_EVENTS = 4
 
 SYMBOLS = ("chunkkv_plan", "chunkkv_workspace_bytes", "chunkkv_score", "chunkkv_select",
            "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_decode_workspace_bytes",
-           "chunkkv_decode_attention", "chunkkv_last_error")
+           "chunkkv_decode_attention", "chunkkv_gather_paged", "chunkkv_last_error")
 
 
 class ChunkKVError(RuntimeError):
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.chunkkv_decode_workspace_bytes.argtypes = [P]
         L.chunkkv_decode_attention.restype = ctypes.c_int
         L.chunkkv_decode_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.chunkkv_gather_paged.restype = ctypes.c_int
+        L.chunkkv_gather_paged.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
         L.chunkkv_last_error.restype = ctypes.c_char_p
         L.chunkkv_last_error.argtypes = []
         _lib = L
@@ -229,6 +231,15 @@ def select(prob, scores, indices, lengths, stream=None) -> None:
 def gather(prob, k, v, indices, lengths, k_out, v_out, stream=None) -> None:
     _check(lib().chunkkv_gather(prob.ref, _ptr(k), _ptr(v), _ptr(indices), _ptr(lengths),
                                 _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def gather_paged(prob, k, v, indices, lengths, block_table, max_pages: int, page_rows: int, n_pages: int,
+                 k_pages, v_pages, stream=None) -> None:
+    """chunkkv_gather_paged: the kept rows written into pool pages
+    [n_pages][page_rows][head_dim] listed by block_table [B * H_kv][max_pages]."""
+    _check(lib().chunkkv_gather_paged(prob.ref, _ptr(k), _ptr(v), _ptr(indices), _ptr(lengths),
+                                      _ptr(block_table), max_pages, page_rows, n_pages, _ptr(k_pages),
+                                      _ptr(v_pages), _stream(stream)))
 
 
 def decode_workspace_bytes(prob: ProblemHandle) -> int:

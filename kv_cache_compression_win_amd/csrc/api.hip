@@ -18,6 +18,7 @@
 #include "chunkkv.h"
 #include "chunkkv_internal.h"
 #include "decode_internal.h"
+#include "paged_internal.h"
 
 namespace {
 
@@ -496,6 +497,63 @@ int chunkkv_gather(const chunkkv_problem* p, const void* k, const void* v, const
   const hipError_t e = run_gather(pl, 1, &k, &v, &k_out, &v_out, &blk, indices, lengths,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int chunkkv_gather_paged(const chunkkv_problem* p, const void* k, const void* v, const int32_t* indices,
+                         const int32_t* lengths, const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                         int64_t n_pages, void* k_pages, void* v_pages, void* stream) {
+  Plan pl;
+  const int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if (!k || !v || !indices || !lengths || !block_table || !k_pages || !v_pages)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "k, v, indices, lengths, block_table, k_pages and v_pages must be non-NULL");
+  if (page_rows < 1 || max_pages < 1 || n_pages < 1)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "page_rows, max_pages and n_pages must be >= 1 (got %d, %d, %lld)",
+                page_rows, max_pages, static_cast<long long>(n_pages));
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pages) || !aligned16(v_pages))
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "K/V buffers and pages must be 16-byte aligned");
+  for (int b = 0; b < pl.B; ++b) {
+    const int64_t need = (static_cast<int64_t>(pl.seq[b].L_cap) + page_rows - 1) / page_rows;
+    if (need > max_pages)
+      return fail(CHUNKKV_ERR_INVALID_ARG, "sequence %d keeps up to %d rows: needs %lld pages of %d rows, max_pages is %d",
+                  b, pl.seq[b].L_cap, static_cast<long long>(need), page_rows, max_pages);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    PagedParams P{};
+    P.k = k;
+    P.v = v;
+    P.kp = k_pages;
+    P.vp = v_pages;
+    P.indices = indices;
+    P.lengths = lengths;
+    P.block_table = block_table;
+    P.n_seqs = nb;
+    P.H_kv = pl.Hkv;
+    P.page_rows = page_rows;
+    P.max_pages = max_pages;
+    P.n_pages = n_pages;
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.tok0[i] = sq.tok0;
+      P.T[i] = sq.T;
+      P.L_cap[i] = sq.L_cap;
+      P.len_off[i] = (b0 + i) * pl.Hkv;
+      P.item0[i] = items;
+      P.blocks_per_head[i] = (sq.L_cap + kGatherRows - 1) / kGatherRows;
+      P.index_off[i] = sq.index_off;
+      items += pl.Hkv * P.blocks_per_head[i];
+    }
+    P.item0[nb] = items;
+    P.row_bytes = pl.d * pl.eb;
+    P.kv_st_bytes = pl.kv_st * pl.eb;
+    P.kv_sh_bytes = pl.kv_sh * pl.eb;
+    const hipError_t e = launch_gather_paged(P, items, s);
+    if (e != hipSuccess) return hip_fail(e, "paged gather launch");
+  }
   return ok();
 }
 

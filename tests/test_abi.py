@@ -112,3 +112,24 @@ def test_entry_points_validate_before_launch():
     small_ws = args[:8] + (16,) + args[9:]
     assert L.chunkkv_compress_layers(p.ref, 2, 2, *(bad_q[:8] + (16,) + bad_q[9:])) == ck.ERR_WORKSPACE
     assert L.chunkkv_compress_layers(p.ref, 2, 1, *small_ws) == ck.ERR_WORKSPACE
+
+
+def test_gather_paged_validates_before_launch():
+    # The paged gather's checks are host-side too: NULL buffers, empty pages,
+    # a block table too short for the longest kept run, misaligned pages.
+    L = ck.lib()
+    p = _p()
+    dummy = 1 << 20
+    l_cap = max(int(x) for x in ck.plan(p)["l_cap"])
+    rows = 16
+    need = -(-l_cap // rows)
+
+    def call(table=dummy, max_pages=need, page_rows=rows, n_pages=64, kp=dummy):
+        return L.chunkkv_gather_paged(p.ref, dummy, dummy, dummy, dummy, table, max_pages, page_rows,
+                                      n_pages, kp, dummy, None)
+
+    assert call(table=None) == ck.ERR_INVALID_ARG
+    assert call(page_rows=0) == ck.ERR_INVALID_ARG
+    assert call(n_pages=0) == ck.ERR_INVALID_ARG
+    assert call(max_pages=need - 1) == ck.ERR_INVALID_ARG
+    assert call(kp=dummy + 4) == ck.ERR_UNSUPPORTED
