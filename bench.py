@@ -118,10 +118,32 @@ def copy_peak(n: int, start, stop, step_gbps: float, reps: int = 5):
             "step_hbm_frac": step_gbps / gbps}
 
 
+def graph_time_us(fn, args, start, stop, n_in=20):
+    """Device time of one fn() call in microseconds: n_in calls captured in a
+    HIP graph (fn must only launch kernels), the graph replayed args.steps
+    times, so host launch costs do not enter."""
+    import torch
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        for _ in range(n_in):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (args.steps * n_in) * 1e3
+
+
 def decode_context(wl, cache, prob, bufs, args, start, stop):
     """Decode attention of one new query per query head over layer 0's
     compacted cache, against the same kernel over that layer's full cache (every
-    token kept: l_max = T), per layer."""
+    token kept: l_max = T), per layer, device time from graph replays."""
     import torch
     from kv_cache_compression_win_amd import chunkkv as ck
     B, Hq, d = len(wl.seq_lens), wl.n_q_heads, wl.head_dim
@@ -133,15 +155,8 @@ def decode_context(wl, cache, prob, bufs, args, start, stop):
     def timed(p, k_out, v_out, lengths):
         ws_n = ck.decode_workspace_bytes(p)
         ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
-        for _ in range(args.warmup):
-            ck.decode_attention(p, q, k_out, v_out, lengths, out, ws, ws_n)
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            ck.decode_attention(p, q, k_out, v_out, lengths, out, ws, ws_n)
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps * 1e3
+        return graph_time_us(lambda: ck.decode_attention(p, q, k_out, v_out, lengths, out, ws, ws_n),
+                             args, start, stop)
 
     nh = B * wl.n_kv_heads
     lens_c = bufs.lengths[:nh]
@@ -164,7 +179,8 @@ def decode_context(wl, cache, prob, bufs, args, start, stop):
 def paged_context(wl, cache, prob, bufs, args, start, stop, page_rows=256):
     """Layer 0's compaction written into pool pages of page_rows rows through a
     shuffled block table (the PagedAttention block layout, Kara page,
-    section 2), against the contiguous gather of the same layer."""
+    section 2), against the contiguous gather of the same layer; device time
+    from graph replays."""
     import torch
     from kv_cache_compression_win_amd import chunkkv as ck
     from kv_cache_compression_win_amd import accounting
@@ -182,15 +198,7 @@ def paged_context(wl, cache, prob, bufs, args, start, stop, page_rows=256):
     k0, v0 = cache["k"][0], cache["v"][0]
 
     def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            fn()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps * 1e3
+        return graph_time_us(fn, args, start, stop)
 
     us_p = timed(lambda: ck.gather_paged(prob, k0, v0, idx, lens, table, max_pages, page_rows, n_pages, kp, vp))
     us_c = timed(lambda: ck.gather(prob, k0, v0, idx, lens, ko, vo))

@@ -7,7 +7,8 @@
 // Split over the rows (flash-decoding style): work item = (sequence, KV head,
 // block of rows), walked kDecRows rows at a time with a running maximum and
 // sum of exponentials (the value sums rescaled when the maximum grows).  Per
-// step, for up to kDecQ query heads of the group at a time: every row's logit
+// step, for up to 8 query heads of the group at a time (4 when the group has
+// at most 4, with half the accumulators): every row's logit
 // (a team of threads per key row, partial dot products added by a butterfly
 // inside the team; the queries in LDS), the step's weights (one lane per row),
 // and the value sums (consecutive threads read consecutive 16-byte pieces of
@@ -37,17 +38,18 @@ __device__ __forceinline__ void widen16(const u32x4 raw, float (&f)[16 / EB]) {
   }
 }
 
-template <int EB>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams P) {
+// QN: query heads per pass (4 or 8), a multiple of the waves per workgroup
+template <int EB, int QN>
+__global__ __launch_bounds__(kThreads, 2) void decode_partial_kernel(const DecodeParams P) {
   constexpr int EPP = 16 / EB;                   // elements per 16-byte piece
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
   const int d = P.d, pieces = P.row_bytes >> 4;
-  float* q_l = smem;                             // [kDecQ][d]
-  float* p_l = q_l + kDecQ * d;                  // [kDecRows][kDecQ] logits, then weights
-  float* acc_l = p_l + kDecRows * kDecQ;         // [subsets][kDecQ][d] partial value sums
-  __shared__ float red[kThreads / 64][kDecQ];
-  __shared__ float res[kDecQ];
+  float* q_l = smem;                             // [QN][d]
+  float* p_l = q_l + QN * d;                  // [kDecRows][QN] logits, then weights
+  float* acc_l = p_l + kDecRows * QN;         // [subsets][QN][d] partial value sums
+  __shared__ float red[kThreads / 64][QN];
+  __shared__ float res[QN];
 
   int item = blockIdx.x;
   int b = 0;
@@ -64,8 +66,41 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
   const int subsets = kThreads / pieces;         // value-phase row subsets
   const int pc_v = tid % pieces, sub = tid / pieces;
 
-  for (int g0 = 0; g0 < P.G; g0 += kDecQ) {
-    const int nq = min(kDecQ, P.G - g0);
+  // logits: a team of TS threads per key row (TS = 4, 2 or 1 dividing the
+  // piece count), each thread a run of ppt consecutive 16-byte pieces,
+  // partial dot products added by a butterfly inside the team; at most one
+  // row per thread and step, since kThreads / TS >= kDecRows
+  const int TS = (pieces % 4 == 0) ? 4 : ((pieces % 2 == 0) ? 2 : 1);
+  const int ppt = pieces / TS, tp = tid % TS, kr_row = tid / TS;
+  // register copies of a step's key pieces (the first kKMax of this thread's
+  // run) and value pieces (the first kVMax rows of this thread's subset);
+  // wider rows read the rest from memory where they are used
+  constexpr int kKMax = 4, kVMax = 4;
+  auto load_step = [&](int c0, u32x4 (&kr)[kKMax], u32x4 (&vr)[kVMax]) {
+    const int rows = min(kDecRows, r_end - c0);
+    const char* kb = static_cast<const char*>(P.k) + (head0 + c0) * P.row_bytes;
+    const char* vb = static_cast<const char*>(P.v) + (head0 + c0) * P.row_bytes;
+    if (kr_row < rows) {
+      const u32x4* row = reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(kr_row) * P.row_bytes);
+#pragma unroll
+      for (int k = 0; k < kKMax; ++k)
+        if (k < ppt) kr[k] = row[tp * ppt + k];
+    }
+    if (sub < subsets) {
+#pragma unroll
+      for (int t = 0; t < kVMax; ++t) {
+        const int i = sub + t * subsets;
+        if (i < rows) vr[t] = reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc_v];
+      }
+    }
+  };
+
+  for (int g0 = 0; g0 < P.G; g0 += QN) {
+    const int nq = min(QN, P.G - g0);
+    // the first step's rows are requested before the queries, so the two
+    // round trips overlap
+    u32x4 kc[kKMax], vc[kVMax], kn[kKMax], vn[kVMax];
+    load_step(r_begin, kc, vc);
     // the queries of this pass, widened to fp32
     for (int e = tid; e < nq * d; e += kThreads) {
       const int g = e / d, j = e - g * d;
@@ -77,58 +112,49 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     __syncthreads();
     // running maximum and sum of exponentials of the block's rows so far, and
     // this thread's unnormalised value sums (rescaled when the maximum grows)
-    float m_run[kDecQ], l_run[kDecQ], a[kDecQ][EPP];
+    float m_run[QN], l_run[QN], a[QN][EPP];
 #pragma unroll
-    for (int g = 0; g < kDecQ; ++g) {
+    for (int g = 0; g < QN; ++g) {
       m_run[g] = -INFINITY;
       l_run[g] = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPP; ++e) a[g][e] = 0.0f;
     }
-    // logits: a team of TS threads per key row (TS = 4, 2 or 1 dividing the
-    // piece count), each thread a run of consecutive 16-byte pieces, partial
-    // dot products added by a butterfly inside the team
-    const int TS = (pieces % 4 == 0) ? 4 : ((pieces % 2 == 0) ? 2 : 1);
-    const int ppt = pieces / TS, tp = tid % TS;
     for (int c0 = r_begin; c0 < r_end; c0 += kDecRows) {
       const int rows = min(kDecRows, r_end - c0);
+      const bool more = c0 + kDecRows < r_end;
+      if (more) load_step(c0 + kDecRows, kn, vn);   // next step's rows in flight during this one
       const char* kb = static_cast<const char*>(P.k) + (head0 + c0) * P.row_bytes;
       const char* vb = static_cast<const char*>(P.v) + (head0 + c0) * P.row_bytes;
-      // this step's value pieces are loaded first: they do not depend on the
-      // weights, so their latency overlaps the logits
-      constexpr int kVMax = 4;   // rows per subset held in registers; more rows are read in the value phase
-      u32x4 vr[kVMax];
-      if (sub < subsets) {
+      {
+        float x[QN];
 #pragma unroll
-        for (int t = 0; t < kVMax; ++t) {
-          const int i = sub + t * subsets;
-          if (i < rows) vr[t] = reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc_v];
-        }
-      }
-      for (int r = tid / TS; r < rows; r += kThreads / TS) {
-        const u32x4* kr = reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(r) * P.row_bytes);
-        float x[kDecQ];
+        for (int g = 0; g < QN; ++g) x[g] = 0.0f;
+        if (kr_row < rows) {
+          const u32x4* kr = reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(kr_row) * P.row_bytes);
+          auto dot = [&](const u32x4 raw, int pc) {
+            float f[EPP];
+            widen16<EB>(raw, f);
 #pragma unroll
-        for (int g = 0; g < kDecQ; ++g) x[g] = 0.0f;
-        for (int k = 0; k < ppt; ++k) {
-          const int pc = tp * ppt + k;
-          float f[EPP];
-          widen16<EB>(kr[pc], f);
+            for (int g = 0; g < QN; ++g) {
+              if (g < nq) {
+                const float* qg = q_l + g * d + pc * EPP;
 #pragma unroll
-          for (int g = 0; g < kDecQ; ++g) {
-            if (g < nq) {
-              const float* qg = q_l + g * d + pc * EPP;
-#pragma unroll
-              for (int e = 0; e < EPP; ++e) x[g] = fmaf(f[e], qg[e], x[g]);
+                for (int e = 0; e < EPP; ++e) x[g] = fmaf(f[e], qg[e], x[g]);
+              }
             }
-          }
+          };
+#pragma unroll
+          for (int k = 0; k < kKMax; ++k)
+            if (k < ppt) dot(kc[k], tp * ppt + k);
+          for (int k = kKMax; k < ppt; ++k) dot(kr[tp * ppt + k], tp * ppt + k);
         }
         for (int o = TS >> 1; o > 0; o >>= 1)
 #pragma unroll
-          for (int g = 0; g < kDecQ; ++g) x[g] += __shfl_xor(x[g], o, 64);
-        if (tp == 0)
+          for (int g = 0; g < QN; ++g) x[g] += __shfl_xor(x[g], o, 64);
+        if (tp == 0 && kr_row < rows)
 #pragma unroll
-          for (int g = 0; g < kDecQ; ++g) p_l[r * kDecQ + g] = x[g] * P.inv_sqrt_d;
+          for (int g = 0; g < QN; ++g) p_l[kr_row * QN + g] = x[g] * P.inv_sqrt_d;
       }
       __syncthreads();
       // each wave takes query heads wave, wave + 4 (one lane per row of the
@@ -138,18 +164,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         const int lane = tid & 63, wave = tid >> 6;
         const bool live = lane < rows;
 #pragma unroll
-        for (int gg = 0; gg < kDecQ / (kThreads / 64); ++gg) {
+        for (int gg = 0; gg < QN / (kThreads / 64); ++gg) {
           const int g = wave + gg * (kThreads / 64);
-          const float x = (live && g < nq) ? p_l[lane * kDecQ + g] : -INFINITY;
+          const float x = (live && g < nq) ? p_l[lane * QN + g] : -INFINITY;
           float m = x;
 #pragma unroll
           for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
           float mr = m_run[0];   // m_run[g] without indexing the register array by a lane-varying value
 #pragma unroll
-          for (int gi = 1; gi < kDecQ; ++gi) mr = gi == g ? m_run[gi] : mr;
+          for (int gi = 1; gi < QN; ++gi) mr = gi == g ? m_run[gi] : mr;
           const float mn = fmaxf(mr, m);
           const float pw = (live && g < nq) ? expf(x - mn) : 0.0f;
-          p_l[lane * kDecQ + g] = pw;
+          p_l[lane * QN + g] = pw;
           float sc = pw;
 #pragma unroll
           for (int o = 32; o > 0; o >>= 1) sc += __shfl_xor(sc, o, 64);
@@ -160,9 +186,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         }
       }
       __syncthreads();
-      float f[kDecQ];
+      float f[QN];
 #pragma unroll
-      for (int g = 0; g < kDecQ; ++g) {
+      for (int g = 0; g < QN; ++g) {
         const float mn = res[g];
         f[g] = m_run[g] == -INFINITY ? 0.0f : expf(m_run[g] - mn);
         l_run[g] = l_run[g] * f[g] + red[0][g];
@@ -171,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
       // value sums: thread (subset, piece) adds rows subset, subset + subsets, ...
       if (sub < subsets) {
 #pragma unroll
-        for (int g = 0; g < kDecQ; ++g)
+        for (int g = 0; g < QN; ++g)
 #pragma unroll
           for (int e = 0; e < EPP; ++e) a[g][e] *= f[g];
 #pragma unroll
@@ -179,10 +205,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
           const int i = sub + t * subsets;
           if (i < rows) {
             float fv[EPP];
-            widen16<EB>(vr[t], fv);
+            widen16<EB>(vc[t], fv);
 #pragma unroll
-            for (int g = 0; g < kDecQ; ++g) {
-              const float p = p_l[i * kDecQ + g];
+            for (int g = 0; g < QN; ++g) {
+              const float p = p_l[i * QN + g];
 #pragma unroll
               for (int e = 0; e < EPP; ++e) a[g][e] = fmaf(p, fv[e], a[g][e]);
             }
@@ -192,28 +218,34 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
           float fv[EPP];
           widen16<EB>(reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(i) * P.row_bytes)[pc_v], fv);
 #pragma unroll
-          for (int g = 0; g < kDecQ; ++g) {
-            const float p = p_l[i * kDecQ + g];
+          for (int g = 0; g < QN; ++g) {
+            const float p = p_l[i * QN + g];
 #pragma unroll
             for (int e = 0; e < EPP; ++e) a[g][e] = fmaf(p, fv[e], a[g][e]);
           }
         }
       }
-      __syncthreads();   // p_l, res and red are rewritten by the next chunk
+      __syncthreads();   // p_l, res and red are rewritten by the next step
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < kKMax; ++k) kc[k] = kn[k];
+#pragma unroll
+        for (int t = 0; t < kVMax; ++t) vc[t] = vn[t];
+      }
     }
     if (sub < subsets)
 #pragma unroll
-      for (int g = 0; g < kDecQ; ++g)
+      for (int g = 0; g < QN; ++g)
         if (g < nq)
 #pragma unroll
-          for (int e = 0; e < EPP; ++e) acc_l[(sub * kDecQ + g) * d + pc_v * EPP + e] = a[g][e];
+          for (int e = 0; e < EPP; ++e) acc_l[(sub * QN + g) * d + pc_v * EPP + e] = a[g][e];
     __syncthreads();
     // the block's partial for each query head of the pass: (max, sum, value sums)
     float* part = P.part + ((P.part_off[b] + static_cast<int64_t>(h) * nblk + blk) * P.G + g0) * (d + 2);
     for (int e = tid; e < nq * d; e += kThreads) {
       const int g = e / d, j = e - g * d;
       float s = 0.0f;
-      for (int u = 0; u < subsets; ++u) s += acc_l[(u * kDecQ + g) * d + j];
+      for (int u = 0; u < subsets; ++u) s += acc_l[(u * QN + g) * d + j];
       part[g * (d + 2) + 2 + j] = s;
     }
     if (tid < nq) {
@@ -288,13 +320,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     const int sub = e / d, j = e - sub * d;
     float s = 0.0f;
     int k = sub;
-    for (; k + 3 * S < nb; k += 4 * S) {   // four independent loads in flight
-      const float a0 = part[k * stride + 2 + j], a1 = part[(k + S) * stride + 2 + j];
-      const float a2 = part[(k + 2 * S) * stride + 2 + j], a3 = part[(k + 3 * S) * stride + 2 + j];
-      s = fmaf(w_l[k], a0, s);
-      s = fmaf(w_l[k + S], a1, s);
-      s = fmaf(w_l[k + 2 * S], a2, s);
-      s = fmaf(w_l[k + 3 * S], a3, s);
+    constexpr int kInFlight = 8;             // independent loads in flight per thread
+    for (; k + (kInFlight - 1) * S < nb; k += kInFlight * S) {
+      float x[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) x[u] = part[(k + u * S) * stride + 2 + j];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) s = fmaf(w_l[k + u * S], x[u], s);
     }
     for (; k < nb; k += S) s = fmaf(w_l[k], part[k * stride + 2 + j], s);
     sub_l[sub * d + j] = s;
@@ -311,15 +343,18 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
 
 size_t decode_lds_bytes(const DecodeParams& p) {
   const int subsets = kThreads / (p.row_bytes >> 4);
-  return (static_cast<size_t>(kDecQ) * p.d + static_cast<size_t>(kDecRows) * kDecQ +
-          static_cast<size_t>(subsets) * kDecQ * p.d) * sizeof(float);
+  const size_t qn = p.G <= 4 ? 4 : kDecQ;   // query heads per pass of the launched variant
+  return (qn * p.d + static_cast<size_t>(kDecRows) * qn + static_cast<size_t>(subsets) * qn * p.d) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int n_items, int n_heads_out, hipStream_t s) {
   const size_t lds = decode_lds_bytes(p);
-  hipError_t e = p.elem_bytes == 4
-                     ? launch1(decode_partial_kernel<4>, dim3(n_items), dim3(kThreads), lds, s, p)
-                     : launch1(decode_partial_kernel<2>, dim3(n_items), dim3(kThreads), lds, s, p);
+  // a group of at most 4 query heads takes the variant with half the value
+  // accumulators (fewer registers, more workgroups per CU)
+  const bool q4 = p.G <= 4;
+  void (*kern)(DecodeParams) = p.elem_bytes == 4 ? (q4 ? decode_partial_kernel<4, 4> : decode_partial_kernel<4, kDecQ>)
+                                                  : (q4 ? decode_partial_kernel<2, 4> : decode_partial_kernel<2, kDecQ>);
+  hipError_t e = launch1(kern, dim3(n_items), dim3(kThreads), lds, s, p);
   if (e != hipSuccess) return e;
   int nbh = 1;
   for (int i = 0; i < p.n_seqs; ++i) nbh = nbh > p.blocks_per_head[i] ? nbh : p.blocks_per_head[i];
