@@ -222,7 +222,7 @@ int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t 
 
 /*
  * Workspace needed by chunkkv_decode_attention for problem p: per-block
- * partials of every (sequence, KV head, block of 64 kept rows, query head).
+ * partials of every (sequence, KV head, block of kept rows, query head).
  * Host only.  Returns 0 on invalid input.
  */
 size_t chunkkv_decode_workspace_bytes(const chunkkv_problem *p);
@@ -235,14 +235,16 @@ size_t chunkkv_decode_workspace_bytes(const chunkkv_problem *p);
  * (Kara eq. (1)); the output is the weighted sum of the kept value rows.
  * The new token's own key and value are not included (an engine appends
  * them); a head with no kept rows gives zeros.
- *   q_dec         DEVICE [n_seqs][n_q_heads][head_dim], the problem's dtype
+ *   q_dec         DEVICE [n_seqs][n_q_heads][head_dim], the problem's dtype,
+ *                 16-byte aligned
  *   k_out, v_out  DEVICE compacted caches as written by chunkkv_gather
  *                 (rows index_off[b] + h * L_cap_b + i), 16-byte aligned
  *   lengths       DEVICE int32 [n_seqs * n_kv_heads], as written by
  *                 chunkkv_select (other values are clamped into [0, L_cap_b])
  *   out           DEVICE fp32 [n_seqs][n_q_heads][head_dim]
- *   workspace     DEVICE scratch of >= chunkkv_decode_workspace_bytes(p) bytes
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ *   workspace     DEVICE scratch of >= chunkkv_decode_workspace_bytes(p)
+ *                 bytes, 16-byte aligned
+ * Errors: INVALID_ARG, UNSUPPORTED (incl. misaligned buffers), WORKSPACE, HIP.
  */
 int chunkkv_decode_attention(const chunkkv_problem *p, const void *q_dec, const void *k_out,
                              const void *v_out, const int32_t *lengths, float *out,

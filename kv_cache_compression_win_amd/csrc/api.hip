@@ -304,16 +304,19 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
   return hipSuccess;
 }
 
-// Kept rows per decode work item: a multiple of kDecRows giving about
-// kDecodeBlocks work items over the whole problem (the blocks' partials are
+// Kept rows per decode work item: a multiple of the item's step giving about
+// kDecodeBlocks workgroup items (kDecodeWaveItems wave items) over the whole problem (the blocks' partials are
 // merged per query head), so short caches still spread over the GPU and long
 // ones keep the merge short.
 constexpr int64_t kDecodeBlocks = 512;
 int decode_rows_per_block(const Plan& pl) {
   int64_t rows = 0;
   for (const Seq& sq : pl.seq) rows += static_cast<int64_t>(pl.Hkv) * sq.L_cap;
-  const int64_t per = std::max<int64_t>((rows + kDecodeBlocks - 1) / kDecodeBlocks, kDecRows);
-  return static_cast<int>(std::min<int64_t>(round_up(per, kDecRows), int64_t{1} << 30));
+  const bool wave = decode_wave_path(pl.d * pl.eb);
+  const int64_t items = wave ? kDecodeWaveItems : kDecodeBlocks;
+  const int64_t step = wave ? kWaveRows : kDecRows;
+  const int64_t per = std::max<int64_t>((rows + items - 1) / items, step);
+  return static_cast<int>(std::min<int64_t>(round_up(per, step), int64_t{1} << 30));
 }
 
 // Scores of nl scoring layers: chunk partials then the log-sum-exp combine,
@@ -645,7 +648,7 @@ size_t chunkkv_decode_workspace_bytes(const chunkkv_problem* p) {
   const int rpb = decode_rows_per_block(pl);
   int64_t blocks = 0;
   for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + rpb - 1) / rpb);
-  return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + 2) * sizeof(float));
+  return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + kPartHead) * sizeof(float));
 }
 
 int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const void* k_out, const void* v_out,
@@ -656,9 +659,9 @@ int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const 
   if (rc) return rc;
   if (!q_dec || !k_out || !v_out || !lengths || !out)
     return fail(CHUNKKV_ERR_INVALID_ARG, "q_dec, k_out, v_out, lengths and out must be non-NULL");
-  if (!aligned16(k_out) || !aligned16(v_out) || reinterpret_cast<uintptr_t>(q_dec) % pl.eb ||
-      reinterpret_cast<uintptr_t>(out) % 4)
-    return fail(CHUNKKV_ERR_UNSUPPORTED, "k_out and v_out must be 16-byte aligned");
+  if (!aligned16(q_dec) || !aligned16(k_out) || !aligned16(v_out) || reinterpret_cast<uintptr_t>(out) % 4 ||
+      (workspace && !aligned16(workspace)))
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "q_dec, k_out, v_out and the workspace must be 16-byte aligned");
   const size_t need = chunkkv_decode_workspace_bytes(p);
   if (!workspace || workspace_bytes < need)
     return fail(CHUNKKV_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0,
