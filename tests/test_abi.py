@@ -133,3 +133,23 @@ def test_gather_paged_validates_before_launch():
     assert call(n_pages=0) == ck.ERR_INVALID_ARG
     assert call(max_pages=need - 1) == ck.ERR_INVALID_ARG
     assert call(kp=dummy + 4) == ck.ERR_UNSUPPORTED
+
+
+def test_decode_attention_validates_before_launch():
+    L = ck.lib()
+    p = _p()
+    dummy = 1 << 20
+    need = L.chunkkv_decode_workspace_bytes(p.ref)
+    assert need > 0 and need % 16 == 0
+    args = dict(q=dummy, k=dummy, v=dummy, lens=dummy, out=dummy, ws=dummy, n=need)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.chunkkv_decode_attention(p.ref, a["q"], a["k"], a["v"], a["lens"], a["out"], a["ws"], a["n"],
+                                          None)
+
+    assert call(q=None) == ck.ERR_INVALID_ARG
+    assert call(q=dummy + 2) == ck.ERR_UNSUPPORTED
+    assert call(ws=dummy + 8) == ck.ERR_UNSUPPORTED
+    assert call(n=need - 16) == ck.ERR_WORKSPACE
+    assert call(ws=None) == ck.ERR_WORKSPACE
