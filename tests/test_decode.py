@@ -100,3 +100,33 @@ def test_decode_after_compression_workload():
     wl = kvsynth.WORKLOADS["llama3-8b-1layer-T8192"]
     _run(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.chunk,
          seed=8)
+
+
+@pytest.mark.parametrize("d", [128, 96])   # the one-wave kernel and the workgroup kernel
+def test_decode_graph_replays_match_eager(d):
+    # the call only launches kernels, so it can be captured; every replay
+    # (with eager work and synchronisation between) equals the eager output
+    prob = ck.make_problem(ck.BF16, [5000], [900], 16, 4, d, 16, 10)
+    pl = ck.plan(prob)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(d)
+    k = torch.randn((pl["index_elems"], d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((pl["index_elems"], d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((1, 16, d), generator=g, device="cuda").to(torch.bfloat16)
+    lengths = torch.tensor([pl["l_cap"][0], 1, 0, 333], dtype=torch.int32, device="cuda")
+    ws_n = ck.decode_workspace_bytes(prob)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    eager = torch.empty((1, 16, d), dtype=torch.float32, device="cuda")
+    ck.decode_attention(prob, q, k, v, lengths, eager, ws, ws_n)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        ck.decode_attention(prob, q, k, v, lengths, out, ws, ws_n)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        del scratch

@@ -88,3 +88,35 @@ def test_gather_paged_many_sequences_and_edge_lengths():
     l_cap = ck.plan(prob)["l_cap"]
     lengths = np.array([(0 if i % 3 == 0 else int(l_cap[i // 2])) for i in range(22)], dtype=np.int32)
     _run(ck.BF16, lens, [600] * 11, 2, 128, 64, seed=11, lengths=lengths)
+
+
+def test_gather_paged_graph_replays_match_eager():
+    T, Hkv, d, rows = 3000, 4, 128, 64
+    prob = ck.make_problem(ck.BF16, [T], [500], Hkv, Hkv, d, 16, 10)
+    pl = ck.plan(prob)
+    rng = np.random.default_rng(4)
+    kh = rng.integers(-2**15, 2**15 - 1, size=(T, Hkv, d), dtype=np.int16)
+    vh = rng.integers(-2**15, 2**15 - 1, size=(T, Hkv, d), dtype=np.int16)
+    L = int(pl["l_cap"][0])
+    idx = np.concatenate([np.sort(rng.choice(T, size=L, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    lengths = np.array([L, 7, 0, L // 2], dtype=np.int32)
+    max_pages = -(-L // rows)
+    n_pages = Hkv * max_pages
+    table = rng.permutation(n_pages).astype(np.int32)
+    args = [torch.from_numpy(x).cuda() for x in (kh, vh, idx, lengths, table)]
+    eager_k = torch.full((n_pages, rows, 2 * d), POISON, dtype=torch.uint8, device="cuda")
+    eager_v = torch.full_like(eager_k, POISON)
+    ck.gather_paged(prob, *args, max_pages, rows, n_pages, eager_k, eager_v)
+    torch.cuda.synchronize()
+    kp, vp = torch.empty_like(eager_k), torch.empty_like(eager_v)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        ck.gather_paged(prob, *args, max_pages, rows, n_pages, kp, vp)
+    for rep in range(3):
+        kp.fill_(POISON)
+        vp.fill_(POISON)
+        scratch = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(kp, eager_k) and torch.equal(vp, eager_v), rep
+        del scratch
