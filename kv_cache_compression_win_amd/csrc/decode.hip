@@ -5,17 +5,19 @@
 // eq. (1)); the output is the weighted sum of the kept value rows.
 //
 // Split over the rows (flash-decoding style): work item = (sequence, KV head,
-// block of rows), walked kDecRows rows at a time with a running maximum and
+// block of rows), walked a step of rows at a time with a running maximum and
 // sum of exponentials (the value sums rescaled when the maximum grows).  Per
 // step, for up to 8 query heads of the group at a time (4 when the group has
-// at most 4, with half the accumulators): every row's logit
-// (a team of threads per key row, partial dot products added by a butterfly
-// inside the team; the queries in LDS), the step's weights (one lane per row),
-// and the value sums (consecutive threads read consecutive 16-byte pieces of
-// a value row; per-thread partial sums are added over the row subsets through
-// LDS in a fixed order at the end).  A second kernel merges the blocks of each query head by
-// their (max, sum) and normalises.  Everything is accumulated in fp32 in a
-// fixed order: results are deterministic.
+// at most 4, with half the accumulators): every row's logit (a team of lanes
+// per key row, partial dot products added by a butterfly inside the team;
+// the queries in LDS), the step's weights, and the value sums (consecutive
+// lanes read consecutive 16-byte pieces of a value row; the row subsets'
+// partial sums are added in a fixed order at the end).  Two partial kernels:
+// rows of 16 pieces take one wavefront per item (32-row steps, no workgroup
+// barriers), other widths one workgroup per item (64-row steps).  A merge
+// kernel combines the blocks of each query head by their (max, sum) and
+// normalises.  Everything is accumulated in fp32 in a fixed order: results
+// are deterministic.
 #include "decode_internal.h"
 
 namespace ckv {
