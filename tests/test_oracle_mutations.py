@@ -10,7 +10,8 @@ reversed tie order and ascending sort in TopK (step 4), a short recent window
 anchor layer's cache (Algorithm 2), a bad bf16 widening and swapped key
 strides; in the decode-attention consumer, a dropped 1/sqrt(d), a flipped
 exponent sign, values taken from the keys and every query head reading the
-first query.
+first query; in the paged layout (Python), pages chosen by i mod P, rows by
+i div P, negative page ids kept and rows shifted by one.
 """
 import concurrent.futures
 import os
@@ -71,3 +72,47 @@ def test_every_planted_mistake_is_caught():
             results = list(ex.map(lambda n: _run(n, tmp), MUTATIONS))
     missed = [n for n, rc in results if rc == 0]
     assert not missed, f"pins did not catch: {missed}"
+
+
+# The paged layout is Python: each mistake is planted in a copy of
+# oracle.to_pages compiled in memory, and the page pins of test_oracle.py are
+# run against it in this process.
+PAGE_MUTATIONS = {
+    "page_by_mod": ("page = int(table[i // page_rows])", "page = int(table[i % page_rows])"),
+    "row_by_div": ("pool[page, i % page_rows]", "pool[page, i // page_rows]"),
+    "keeps_negative_ids": ("if 0 <= page < n_pages:", "if page < n_pages:"),
+    "shifted_rows": ("= rows[i]", "= rows[max(i - 1, 0)]"),
+}
+
+
+def _page_pins():
+    import test_oracle as t
+    yield t.test_to_pages_worked_example
+    yield t.test_to_pages_one_large_page_is_the_contiguous_layout
+    for n, p in ((97, 16), (250, 7)):
+        yield lambda n=n, p=p: t.test_to_pages_read_back_through_the_table(n, p)
+    yield t.test_to_pages_skips_out_of_range_page_ids
+
+
+@pytest.mark.parametrize("name", sorted(PAGE_MUTATIONS))
+def test_every_planted_page_layout_mistake_is_caught(name, monkeypatch):
+    import inspect
+    import textwrap
+
+    import numpy as np
+
+    import oracle
+    src = textwrap.dedent(inspect.getsource(oracle.to_pages))
+    a, b = PAGE_MUTATIONS[name]
+    assert src.count(a) == 1, name
+    ns = {"np": np}
+    exec(compile(src.replace(a, b), f"<mutant {name}>", "exec"), ns)
+    monkeypatch.setattr(oracle, "to_pages", ns["to_pages"])
+    caught = False
+    for pin in _page_pins():
+        try:
+            pin()
+        except Exception:   # a failed assertion or an out-of-range write both count
+            caught = True
+            break
+    assert caught, f"mutation {name} passed every page pin"
