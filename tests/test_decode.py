@@ -77,6 +77,9 @@ def _run(dtype, seq_lens, l_max, Hq, Hkv, d, w, c, seed, lengths=None):
     (ck.BF16, 96, 6, 3),       # 12 pieces per row
     (ck.BF16, 8, 4, 1),        # one 16-byte piece per row
     (ck.F32, 256, 4, 2),       # 64 pieces per row
+    (ck.F32, 64, 16, 2),       # one-wave kernel, fp32, 8 query heads per pass
+    (ck.BF16, 96, 24, 3),      # workgroup kernel, 8 query heads per pass
+    (ck.F32, 256, 12, 1),      # workgroup kernel, G = 12: two passes
 ])
 def test_decode_matches_oracle(dtype, d, Hq, Hkv):
     # two sequences whose budgets span several 256-row blocks and a ragged last block
