@@ -244,6 +244,8 @@ size_t chunkkv_decode_workspace_bytes(const chunkkv_problem *p);
  *   out           DEVICE fp32 [n_seqs][n_q_heads][head_dim]
  *   workspace     DEVICE scratch of >= chunkkv_decode_workspace_bytes(p)
  *                 bytes, 16-byte aligned
+ * All buffers belong to the caller; the call allocates nothing and only
+ * launches kernels on `stream`, so it can be captured into a HIP graph.
  * Errors: INVALID_ARG, UNSUPPORTED (incl. misaligned buffers), WORKSPACE, HIP.
  */
 int chunkkv_decode_attention(const chunkkv_problem *p, const void *q_dec, const void *k_out,
@@ -267,6 +269,8 @@ int chunkkv_decode_attention(const chunkkv_problem *p, const void *q_dec, const 
  *                 aligned; only the rows of kept rows are written.  A page id
  *                 outside [0, n_pages) leaves its rows unwritten; pages
  *                 listed twice get the rows of whichever copy lands last.
+ * All buffers belong to the caller; the call allocates nothing and only
+ * launches kernels on `stream`, so it can be captured into a HIP graph.
  * Errors: INVALID_ARG (incl. page_rows, max_pages or n_pages < 1, a table
  * too short for L_cap), UNSUPPORTED, HIP.
  */
