@@ -118,17 +118,32 @@ typedef struct {
 /*
  * Host-only planning: validates the problem and fills the sizes and, when
  * the arrays are non-NULL, the per-sequence offsets (HOST arrays of n_seqs
- * entries) and L_cap_b = min(T_b, floor(L_max_b / c) * c + w).  Touches no
- * device and needs no GPU.
- * Errors: CHUNKKV_ERR_INVALID_ARG / CHUNKKV_ERR_UNSUPPORTED, nothing written.
+ * entries) and L_cap_b = min(T_b, floor(L_max_b / c) * c + w).  The sizes
+ * follow ChunkKV page, section 4.1, Algorithm 1: step 2 fixes the chunk count
+ * C_b = ceil(T_b / c) (the last chunk may be short, so scores_elems counts
+ * C_b per head), step 4 the number of kept chunks k_b = floor(L_max_b / c),
+ * and step 5 the w recent tokens that are always kept, so a head keeps at
+ * most L_cap_b rows (index_elems counts L_cap_b per head).  Touches no device
+ * and needs no GPU.
+ *   p          HOST problem (read during the call only)
+ *   out        HOST sizes out (required)
+ *   score_off, index_off, l_cap  HOST int64 [n_seqs] out, each may be NULL
+ * Errors: CHUNKKV_ERR_INVALID_ARG / CHUNKKV_ERR_UNSUPPORTED (out NULL, or
+ * the problem outside the method's domain or this library's support),
+ * nothing written.
  */
 int chunkkv_plan(const chunkkv_problem *p, chunkkv_sizes *out, int64_t *score_off,
                  int64_t *index_off, int64_t *l_cap);
 
 /*
  * Workspace needed by chunkkv_compress_layers to score `n_score_layers`
- * layers per launch (1 <= n_score_layers; more layers per launch means fewer
- * launches).  Host only.  Returns 0 on invalid input.
+ * layers per launch (1 <= n_score_layers, counted up to 32; more layers per
+ * launch means fewer launches).  Its size follows from the same quantities as
+ * chunkkv_plan (ChunkKV page, section 4.1, Algorithm 1 step 2: C_b chunks per
+ * head; step 3: the chunk scores are sums of softmax rows normalised over
+ * all T_b keys, whose per-row statistics and, where the kernels keep them,
+ * per-row chunk partials live here between launches).  Host only.  Returns 0
+ * on invalid input (a NULL or invalid problem, n_score_layers < 1).
  */
 size_t chunkkv_workspace_bytes(const chunkkv_problem *p, int32_t n_score_layers);
 

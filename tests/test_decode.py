@@ -31,15 +31,23 @@ def _bits(a, dtype):
     return kvsynth.bf16_bits(t), t
 
 
-def _run(dtype, seq_lens, l_max, Hq, Hkv, d, w, c, seed, lengths=None):
+def _run(dtype, seq_lens, l_max, Hq, Hkv, d, w, c, seed, lengths=None, rows=None):
+    """Decode over a host-written compacted cache checked against the oracle.
+    rows(rng, pl, q) may give the (k, v) float arrays of all index_elems rows
+    (default: N(0, 2) keys, N(0, 1) values); q is the [B, Hq, d] query array."""
     rng = np.random.default_rng(seed)
     prob = ck.make_problem(dtype, seq_lens, l_max, Hq, Hkv, d, w, c)
     pl = ck.plan(prob)
-    rows = pl["index_elems"]
+    n_rows = pl["index_elems"]
     B, G = len(seq_lens), Hq // Hkv
-    kh, kt = _bits(rng.standard_normal((rows, d)) * 2, dtype)
-    vh, vt = _bits(rng.standard_normal((rows, d)), dtype)
-    qh, qt = _bits(rng.standard_normal((B, Hq, d)), dtype)
+    q_f = rng.standard_normal((B, Hq, d))
+    if rows is None:
+        k_f, v_f = rng.standard_normal((n_rows, d)) * 2, rng.standard_normal((n_rows, d))
+    else:
+        k_f, v_f = rows(rng, pl, q_f)
+    kh, kt = _bits(k_f, dtype)
+    vh, vt = _bits(v_f, dtype)
+    qh, qt = _bits(q_f, dtype)
     if lengths is None:
         lengths = np.array([rng.integers(0, pl["l_cap"][b] + 1) for b in range(B) for _ in range(Hkv)],
                            dtype=np.int32)
@@ -69,6 +77,36 @@ def _run(dtype, seq_lens, l_max, Hq, Hkv, d, w, c, seed, lengths=None):
     return got
 
 
+# Work split of the decode call, as the library documents it: rows of 16
+# pieces of 16 bytes take the one-wave kernel (about 2048 items, 32-row
+# steps), other rows the workgroup kernel (about 512 items, 64-row steps);
+# an item's block is a multiple of the step.
+WAVE_ITEMS, WAVE_ROWS = 2048, 32
+WG_ITEMS, WG_ROWS = 512, 64
+
+
+def _steps_per_item(prob, dtype, d, Hq, Hkv):
+    """Steps per full work item of the decode call on problem prob; the
+    workspace size the library asks for must match the same split."""
+    pl = ck.plan(prob)
+    n_rows = Hkv * sum(pl["l_cap"])
+    wave = d * (4 if dtype == ck.F32 else 2) == 256
+    items, step = (WAVE_ITEMS, WAVE_ROWS) if wave else (WG_ITEMS, WG_ROWS)
+    rpb = -(-max(-(-n_rows // items), step) // step) * step
+    blocks = sum(Hkv * -(-lc // rpb) for lc in pl["l_cap"])
+    need = blocks * (Hq // Hkv) * (d + 4) * 4
+    assert ck.decode_workspace_bytes(prob) == -(-need // 256) * 256
+    return rpb // step
+
+
+def _full_or_random_lengths(pl, Hkv, seed):
+    """Every other (sequence, head) keeps all L_cap rows (full work items,
+    every step taken); the rest a random count."""
+    rng = np.random.default_rng(seed)
+    return np.array([pl["l_cap"][b] if (b + h) % 2 == 0 else rng.integers(0, pl["l_cap"][b] + 1)
+                     for b in range(len(pl["l_cap"])) for h in range(Hkv)], dtype=np.int32)
+
+
 @pytest.mark.parametrize("dtype,d,Hq,Hkv", [
     (ck.BF16, 128, 32, 8),     # Llama-3-8B heads (G = 4)
     (ck.BF16, 128, 64, 8),     # 70B-shaped heads (G = 8)
@@ -82,8 +120,107 @@ def _run(dtype, seq_lens, l_max, Hq, Hkv, d, w, c, seed, lengths=None):
     (ck.F32, 256, 12, 1),      # workgroup kernel, G = 12: two passes
 ])
 def test_decode_matches_oracle(dtype, d, Hq, Hkv):
-    # two sequences whose budgets span several 256-row blocks and a ragged last block
+    # two sequences with budgets of a few hundred rows: one step per work
+    # item, a ragged last block per head
     _run(dtype, [4000, 1300], [700, 300], Hq, Hkv, d, 16, 10, seed=d + Hq)
+
+
+def _monotone_rows(direction):
+    """Keys along each head's mean query direction with a strength that rises
+    (direction +1) or falls (-1) over the kept rows: with +1 every step's
+    maximum exceeds the running one (the value sums are rescaled at every step
+    with a finite running maximum), with -1 the first step holds it."""
+    def rows(rng, pl, q):
+        n_rows, d = pl["index_elems"], q.shape[2]
+        k = rng.standard_normal((n_rows, d)) * 0.3
+        v = rng.standard_normal((n_rows, d))
+        B, Hq = q.shape[0], q.shape[1]
+        Hkv = pl["length_elems"] // B
+        G = Hq // Hkv
+        for b in range(B):
+            lc = pl["l_cap"][b]
+            for h in range(Hkv):
+                u = q[b, h * G:(h + 1) * G].mean(axis=0)
+                u = u / np.linalg.norm(u)
+                ramp = np.linspace(0.0, 1.0, lc) if direction > 0 else np.linspace(1.0, 0.0, lc)
+                o = pl["index_off"][b] + h * lc
+                k[o:o + lc] += (6.0 * np.sqrt(d) / 4.0) * ramp[:, None] * u[None, :]
+        return k, v
+    return rows
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,T,l_max,min_steps", [
+    (ck.BF16, 128, 8, 2, 60000, 50000, 2),     # one-wave kernel: 100032 rows, 2 steps of 32
+    (ck.F32, 64, 8, 1, 200000, 190000, 3),     # one-wave kernel, fp32: 3 steps
+    (ck.BF16, 96, 12, 4, 30000, 29000, 4),     # workgroup kernel: 116064 rows, 4 steps of 64
+    (ck.F32, 256, 8, 2, 40000, 30000, 2),      # workgroup kernel, 64 pieces per row: 2 steps
+    (ck.BF16, 128, 24, 2, 70000, 69000, 3),    # one-wave kernel, G = 12 (two passes of query heads): 3 steps
+])
+def test_decode_multi_step_items(dtype, d, Hq, Hkv, T, l_max, min_steps):
+    # caches large enough that every full work item walks several steps: the
+    # next step's keys and values are requested during the current one, and
+    # the running maximum and value sums carry over between steps
+    prob = ck.make_problem(dtype, [T], [l_max], Hq, Hkv, d, 16, 10)
+    assert _steps_per_item(prob, dtype, d, Hq, Hkv) >= min_steps
+    pl = ck.plan(prob)
+    _run(dtype, [T], [l_max], Hq, Hkv, d, 16, 10, seed=T + d,
+         lengths=_full_or_random_lengths(pl, Hkv, seed=T))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("d", [128, 96])      # the one-wave kernel and the workgroup kernel
+def test_decode_running_max_moves(direction, d):
+    # logits that rise (or fall) along the kept rows, over several steps per item
+    T, l_max, Hq, Hkv = 80000, 75000, 8, 2
+    prob = ck.make_problem(ck.BF16, [T], [l_max], Hq, Hkv, d, 16, 10)
+    assert _steps_per_item(prob, ck.BF16, d, Hq, Hkv) >= 2
+    pl = ck.plan(prob)
+    lengths = np.array([pl["l_cap"][0]] * Hkv, dtype=np.int32)
+    _run(ck.BF16, [T], [l_max], Hq, Hkv, d, 16, 10, seed=d + direction, lengths=lengths,
+         rows=_monotone_rows(direction))
+
+
+def test_decode_full_cache_of_32k_layer():
+    # layer 0 of the 32-layer 32k stack with every token kept (L_max = T):
+    # 262144 rows over 8 KV heads, 4 steps per one-wave item; the compacted
+    # cache is the layer's K/V made head-major on the host side of the test
+    wl = kvsynth.WORKLOADS["llama3-8b-32layer-T32768"].with_(n_layers=1)
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    T, Hq, Hkv, d = wl.seq_lens[0], wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    prob = ck.make_problem(ck.BF16, [T], [T], Hq, Hkv, d, wl.window, wl.chunk)
+    assert _steps_per_item(prob, ck.BF16, d, Hq, Hkv) == 4
+    k_out = cache["k"][0].permute(1, 0, 2).contiguous().reshape(-1, d)
+    v_out = cache["v"][0].permute(1, 0, 2).contiguous().reshape(-1, d)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    q = torch.randn((1, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    lengths = torch.full((Hkv,), T, dtype=torch.int32, device="cuda")
+    ws_n = ck.decode_workspace_bytes(prob)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, Hq, d), dtype=torch.float32, device="cuda")
+    ck.decode_attention(prob, q, k_out, v_out, lengths, out, ws, ws_n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qh, kh, vh = kvsynth.bf16_bits(q.cpu()), kvsynth.bf16_bits(k_out.cpu()), kvsynth.bf16_bits(v_out.cpu())
+    G = Hq // Hkv
+    for h in range(Hkv):
+        ref = oracle.decode_attention(qh[0, h * G:(h + 1) * G], kh[h * T:(h + 1) * T], vh[h * T:(h + 1) * T])
+        vmax = float(v_out[h * T:(h + 1) * T].abs().max().float())
+        err = np.abs(got[0, h * G:(h + 1) * G] - ref)
+        assert np.all(err <= TOL * (vmax + np.abs(ref))), (h, float(err.max()))
+
+
+def test_decode_70b_shaped_compressed_cache():
+    # the 70B-shaped batch's compacted cache (4 sequences of 131072 / 65536 /
+    # 32768 / 16384 tokens at a 20% budget, 8 KV heads, G = 8): 395088 rows,
+    # 7 steps per one-wave item; synthetic kept rows written on the host
+    wl = kvsynth.WORKLOADS["llama-70b-80layer-4seq"]
+    prob = ck.make_problem(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                           wl.window, wl.chunk)
+    assert _steps_per_item(prob, ck.BF16, wl.head_dim, wl.n_q_heads, wl.n_kv_heads) == 7
+    pl = ck.plan(prob)
+    _run(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.chunk,
+         seed=70, lengths=_full_or_random_lengths(pl, wl.n_kv_heads, seed=70))
 
 
 def test_decode_edge_lengths_and_many_sequences():

@@ -8,6 +8,7 @@ times, the chunk-size sweep and the 70B-shaped batch) check sampled units
 against the oracle and properties on all units.
 """
 import concurrent.futures
+import os
 
 import numpy as np
 import pytest
@@ -21,7 +22,7 @@ from kv_cache_compression_win_amd import chunkkv as ck
 
 pytestmark = pytest.mark.gpu
 
-POOL = concurrent.futures.ThreadPoolExecutor(max_workers=8)
+POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(8, min(16, os.cpu_count() or 8)))
 
 
 def _all_units(case, layers=None):
@@ -225,6 +226,7 @@ def test_graph_capture_replays_match_eager():
     # bit.
     case = random_case(ck.BF16, [4096, 1500], [400, 150], 32, 8, 128, 32, 10, n_layers=4, n_reuse=2,
                        seed=7).run()
+    _all_units(case)            # the eager outputs the replays must equal match the oracle
     ref = case.bufs
     L = case.L
     bufs = ck.Buffers(case.prob, L, case.n_reuse, case.d, torch.bfloat16, "cuda")
@@ -357,20 +359,17 @@ def test_llama3_8b_layer_T8192():
     _all_units(case)
 
 
-def test_llama3_8b_32layer_T32768_sampled():
-    # The workload the benchmark times, in the same launch configuration.
+def test_llama3_8b_32layer_T32768_all_units():
+    # The workload the benchmark times, in the same launch configuration:
+    # every one of its 16 scoring layers x 8 KV heads against the oracle
+    # (about 1 s of host time per unit), each with its reusing layer.
     wl = kvsynth.WORKLOADS["llama3-8b-32layer-T32768"]
     cache = kvsynth.make_cache(wl, device="cuda", seed=0)
     case = Case(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window,
                 wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
     _props_all_units(case)
     _gather_all_layers_on_gpu(case)
-    jobs = {(a, h): POOL.submit(oracle.chunk_scores, case.host_q(a, 0), case.host_kv(case.k, a, 0),
-                                h, case.Hq, case.w, case.c) for a in (0, 30) for h in (0, 7)}
-    for (a, h), fut in jobs.items():
-        s_ref = fut.result()
-        for l in (a, a + 1):
-            check_unit(case, l, 0, h, s_ref=s_ref)
+    _all_units(case)
 
 
 def test_chunk_size_sweep_T16384():
@@ -400,8 +399,12 @@ def test_llama70b_batch_sampled():
                 wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
     _props_all_units(case)
     _gather_all_layers_on_gpu(case)
+    # the oracle on every head of the 16384-token sequence and on sampled
+    # heads of the others (a 131072-token unit costs about 20 s of host time)
+    units = [(a, 3, h) for a in (0, 2) for h in range(case.Hkv)]
+    units += [(0, 2, 3), (2, 2, 6), (0, 1, 1), (2, 0, 5)]
     jobs = {(a, b, h): POOL.submit(oracle.chunk_scores, case.host_q(a, b), case.host_kv(case.k, a, b),
-                                   h, case.Hq, case.w, case.c) for (a, b, h) in ((0, 3, 0), (2, 3, 7), (0, 2, 3))}
+                                   h, case.Hq, case.w, case.c) for (a, b, h) in units}
     for (a, b, h), fut in jobs.items():
         s_ref = fut.result()
         for l in (a, a + 1):
