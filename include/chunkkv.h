@@ -267,6 +267,32 @@ int chunkkv_decode_attention(const chunkkv_problem *p, const void *q_dec, const 
                              const void *v_out, const int32_t *lengths, float *out,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the scratch array chunkkv_decode_attention_static uses (per GPU). */
+#define CHUNKKV_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * chunkkv_decode_attention without a caller workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus the
+ * workspace), same kernels and the same results as chunkkv_decode_attention.
+ * The per-block partials go to a file-scope device array of
+ * CHUNKKV_STATIC_SCRATCH_BYTES (16 MiB) inside the library, one per GPU the
+ * library runs on, held until the process ends.  The call allocates and frees
+ * nothing (no hipMalloc, no allocating library routine); its first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress) and
+ * keeps the address.  Every call on a GPU shares that GPU's array and it
+ * keeps the last call's contents (no call relies on them): calls that
+ * overlap in time on one GPU (other streams, other host threads) race on it
+ * and must be ordered by the caller.
+ * Errors: as chunkkv_decode_attention; CHUNKKV_ERR_WORKSPACE (before anything
+ * is launched) when chunkkv_decode_workspace_bytes(p) exceeds
+ * CHUNKKV_STATIC_SCRATCH_BYTES; CHUNKKV_ERR_HIP when the array's address
+ * cannot be looked up.
+ */
+int chunkkv_decode_attention_static(const chunkkv_problem *p, const void *q_dec, const void *k_out,
+                                    const void *v_out, const int32_t *lengths, float *out,
+                                    void *stream);
+
 /*
  * Paged output: the same copy as chunkkv_gather (ChunkKV page, section 4.1,
  * Algorithm 1 step 6), written into a pool of fixed-size pages of

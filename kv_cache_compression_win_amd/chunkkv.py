@@ -22,7 +22,9 @@ N_PHASE_EVENTS = 4
 
 SYMBOLS = ("chunkkv_plan", "chunkkv_workspace_bytes", "chunkkv_score", "chunkkv_select",
            "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_decode_workspace_bytes",
-           "chunkkv_decode_attention", "chunkkv_gather_paged", "chunkkv_last_error")
+           "chunkkv_decode_attention", "chunkkv_decode_attention_static", "chunkkv_gather_paged",
+           "chunkkv_last_error")
+STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class ChunkKVError(RuntimeError):
@@ -84,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.chunkkv_decode_workspace_bytes.argtypes = [P]
         L.chunkkv_decode_attention.restype = ctypes.c_int
         L.chunkkv_decode_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.chunkkv_decode_attention_static.restype = ctypes.c_int
+        L.chunkkv_decode_attention_static.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.chunkkv_gather_paged.restype = ctypes.c_int
         L.chunkkv_gather_paged.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
         L.chunkkv_last_error.restype = ctypes.c_char_p
@@ -255,6 +259,13 @@ def decode_attention(prob, q_dec, k_out, v_out, lengths, out, workspace, workspa
     compacted cache (out fp32 [n_seqs][n_q_heads][head_dim])."""
     _check(lib().chunkkv_decode_attention(prob.ref, _ptr(q_dec), _ptr(k_out), _ptr(v_out), _ptr(lengths),
                                           _ptr(out), _ptr(workspace), workspace_nbytes, _stream(stream)))
+
+
+def decode_attention_static(prob, q_dec, k_out, v_out, lengths, out, stream=None) -> None:
+    """chunkkv_decode_attention_static: decode_attention with the library's
+    own per-GPU static scratch (STATIC_SCRATCH_BYTES) instead of a workspace."""
+    _check(lib().chunkkv_decode_attention_static(prob.ref, _ptr(q_dec), _ptr(k_out), _ptr(v_out), _ptr(lengths),
+                                                 _ptr(out), _stream(stream)))
 
 
 def compress_layers(prob, n_reuse: int, q_win: Sequence, k: Sequence, v: Sequence, k_out: Sequence,

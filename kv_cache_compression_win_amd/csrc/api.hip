@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -429,6 +430,98 @@ int check_ws(const Plan& pl, const void* ws, size_t ws_bytes, int nl) {
   return CHUNKKV_OK;
 }
 
+size_t decode_ws_bytes(const Plan& pl) {
+  const int rpb = decode_rows_per_block(pl);
+  int64_t blocks = 0;
+  for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + rpb - 1) / rpb);
+  return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + kPartHead) * sizeof(float));
+}
+
+int check_decode_args(const void* q_dec, const void* k_out, const void* v_out, const int32_t* lengths,
+                      const float* out) {
+  if (!q_dec || !k_out || !v_out || !lengths || !out)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "q_dec, k_out, v_out, lengths and out must be non-NULL");
+  if (!aligned16(q_dec) || !aligned16(k_out) || !aligned16(v_out) || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(CHUNKKV_ERR_UNSUPPORTED, "q_dec, k_out, v_out and the workspace must be 16-byte aligned");
+  return CHUNKKV_OK;
+}
+
+// Decode attention with the partial records in `part` (at least
+// decode_ws_bytes(pl) bytes, 16-byte aligned; every record the merge reads is
+// written by the partial kernel of the same call, so its contents on entry
+// do not matter).
+int run_decode(const Plan& pl, const void* q_dec, const void* k_out, const void* v_out, const int32_t* lengths,
+               float* out, float* part, hipStream_t s) {
+  const int rpb = decode_rows_per_block(pl);
+  int64_t part0 = 0;
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    DecodeParams P{};
+    P.q = q_dec;
+    P.k = k_out;
+    P.v = v_out;
+    P.lengths = lengths;
+    P.out = out;
+    P.part = part;
+    P.n_seqs = nb;
+    P.H_q = pl.Hq;
+    P.H_kv = pl.Hkv;
+    P.G = pl.G;
+    P.d = pl.d;
+    P.row_bytes = pl.d * pl.eb;
+    P.elem_bytes = pl.eb;
+    P.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(pl.d)));
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.qseq[i] = b0 + i;
+      P.item0[i] = items;
+      P.blocks_per_head[i] = (sq.L_cap + rpb - 1) / rpb;
+      P.rows_per_block[i] = rpb;
+      P.L_cap[i] = sq.L_cap;
+      P.len_off[i] = (b0 + i) * pl.Hkv;
+      P.index_off[i] = sq.index_off;
+      P.part_off[i] = part0;
+      part0 += static_cast<int64_t>(pl.Hkv) * P.blocks_per_head[i];
+      items += pl.Hkv * P.blocks_per_head[i];
+    }
+    P.item0[nb] = items;
+    if (decode_lds_bytes(P) > 160 * 1024) return fail(CHUNKKV_ERR_UNSUPPORTED, "head_dim too large for decode");
+    const hipError_t e = launch_decode(P, items, nb * pl.Hq, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  return ok();
+}
+
+// ------------------------------------------------------- static scratch --
+// The scratch of chunkkv_decode_attention_static: one array per GPU, held
+// until the process ends.  In host code its name stands for a host-side
+// placeholder, not a device address: only the address hipGetSymbolAddress
+// returns for the current device (looked up once per device, on the first
+// call there) is ever passed to a kernel.
+constexpr size_t kStaticScratchBytes = size_t{CHUNKKV_STATIC_SCRATCH_BYTES};
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+hipError_t static_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch_dev[dev]);
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -645,67 +738,40 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
 size_t chunkkv_decode_workspace_bytes(const chunkkv_problem* p) {
   Plan pl;
   if (make_plan(p, pl)) return 0;
-  const int rpb = decode_rows_per_block(pl);
-  int64_t blocks = 0;
-  for (const Seq& sq : pl.seq) blocks += static_cast<int64_t>(pl.Hkv) * ((sq.L_cap + rpb - 1) / rpb);
-  return align_up(static_cast<size_t>(blocks) * pl.G * (pl.d + kPartHead) * sizeof(float));
+  return decode_ws_bytes(pl);
 }
 
 int chunkkv_decode_attention(const chunkkv_problem* p, const void* q_dec, const void* k_out, const void* v_out,
                              const int32_t* lengths, float* out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   Plan pl;
-  const int rc = make_plan(p, pl);
+  int rc = make_plan(p, pl);
   if (rc) return rc;
-  if (!q_dec || !k_out || !v_out || !lengths || !out)
-    return fail(CHUNKKV_ERR_INVALID_ARG, "q_dec, k_out, v_out, lengths and out must be non-NULL");
-  if (!aligned16(q_dec) || !aligned16(k_out) || !aligned16(v_out) || reinterpret_cast<uintptr_t>(out) % 4 ||
-      (workspace && !aligned16(workspace)))
+  if ((rc = check_decode_args(q_dec, k_out, v_out, lengths, out))) return rc;
+  if (workspace && !aligned16(workspace))
     return fail(CHUNKKV_ERR_UNSUPPORTED, "q_dec, k_out, v_out and the workspace must be 16-byte aligned");
-  const size_t need = chunkkv_decode_workspace_bytes(p);
+  const size_t need = decode_ws_bytes(pl);
   if (!workspace || workspace_bytes < need)
     return fail(CHUNKKV_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0,
                 need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int rpb = decode_rows_per_block(pl);
-  int64_t part0 = 0;
-  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
-    const int nb = std::min(kMaxSeqs, pl.B - b0);
-    DecodeParams P{};
-    P.q = q_dec;
-    P.k = k_out;
-    P.v = v_out;
-    P.lengths = lengths;
-    P.out = out;
-    P.part = static_cast<float*>(workspace);
-    P.n_seqs = nb;
-    P.H_q = pl.Hq;
-    P.H_kv = pl.Hkv;
-    P.G = pl.G;
-    P.d = pl.d;
-    P.row_bytes = pl.d * pl.eb;
-    P.elem_bytes = pl.eb;
-    P.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(pl.d)));
-    int items = 0;
-    for (int i = 0; i < nb; ++i) {
-      const Seq& sq = pl.seq[b0 + i];
-      P.qseq[i] = b0 + i;
-      P.item0[i] = items;
-      P.blocks_per_head[i] = (sq.L_cap + rpb - 1) / rpb;
-      P.rows_per_block[i] = rpb;
-      P.L_cap[i] = sq.L_cap;
-      P.len_off[i] = (b0 + i) * pl.Hkv;
-      P.index_off[i] = sq.index_off;
-      P.part_off[i] = part0;
-      part0 += static_cast<int64_t>(pl.Hkv) * P.blocks_per_head[i];
-      items += pl.Hkv * P.blocks_per_head[i];
-    }
-    P.item0[nb] = items;
-    if (decode_lds_bytes(P) > 160 * 1024) return fail(CHUNKKV_ERR_UNSUPPORTED, "head_dim too large for decode");
-    const hipError_t e = launch_decode(P, items, nb * pl.Hq, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-  }
-  return ok();
+  return run_decode(pl, q_dec, k_out, v_out, lengths, out, static_cast<float*>(workspace),
+                    static_cast<hipStream_t>(stream));
+}
+
+int chunkkv_decode_attention_static(const chunkkv_problem* p, const void* q_dec, const void* k_out,
+                                    const void* v_out, const int32_t* lengths, float* out, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, pl);
+  if (rc) return rc;
+  if ((rc = check_decode_args(q_dec, k_out, v_out, lengths, out))) return rc;
+  const size_t need = decode_ws_bytes(pl);
+  if (need > kStaticScratchBytes)
+    return fail(CHUNKKV_ERR_WORKSPACE, "decode needs %zu bytes of scratch, the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  float* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  return run_decode(pl, q_dec, k_out, v_out, lengths, out, ws, static_cast<hipStream_t>(stream));
 }
 
 const char* chunkkv_last_error(void) { return g_err.c_str(); }

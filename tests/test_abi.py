@@ -153,3 +153,19 @@ def test_decode_attention_validates_before_launch():
     assert call(ws=dummy + 8) == ck.ERR_UNSUPPORTED
     assert call(n=need - 16) == ck.ERR_WORKSPACE
     assert call(ws=None) == ck.ERR_WORKSPACE
+
+
+def test_decode_attention_static_validates_before_launch():
+    # The static-scratch variant rejects, on the host, problems whose decode
+    # partials need more than the library's 16 MiB array, and the same bad
+    # arguments as chunkkv_decode_attention.
+    L = ck.lib()
+    dummy = 1 << 20
+    big = ck.make_problem(ck.BF16, [131072], [131072], 128, 8, 128, 32, 10)   # G = 16, all rows kept
+    assert L.chunkkv_decode_workspace_bytes(big.ref) > ck.STATIC_SCRATCH_BYTES
+    assert L.chunkkv_decode_attention_static(big.ref, dummy, dummy, dummy, dummy, dummy, None) == ck.ERR_WORKSPACE
+    assert "static scratch" in ck.last_error()
+    p = _p()
+    assert L.chunkkv_decode_attention_static(p.ref, None, dummy, dummy, dummy, dummy, None) == ck.ERR_INVALID_ARG
+    assert L.chunkkv_decode_attention_static(p.ref, dummy, dummy + 2, dummy, dummy, dummy, None) == ck.ERR_UNSUPPORTED
+    assert L.chunkkv_decode_attention_static(None, dummy, dummy, dummy, dummy, dummy, None) == ck.ERR_INVALID_ARG
