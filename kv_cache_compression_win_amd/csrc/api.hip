@@ -12,6 +12,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -62,15 +64,32 @@ struct Plan {
   int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
   bool mfma = false;
   bool two_pass = false;   // statistics pass + final-score pass, no chunk partials
+  // exchange mode possible: its longest span (chunks) and the chunks per MFMA group
+  int x_max_span = 0, group_chunks = 0;
   std::vector<Seq> seq;
   int64_t scores_elems = 0, index_elems = 0, length_elems = 0, u_elems = 0, st_elems = 0, lse_elems = 0;
   int64_t kv_st = 0, kv_sh = 0, q_ss = 0, q_sr = 0, q_sh = 0;
-  size_t ws_bytes(int n_layers) const {
-    return align_up(static_cast<size_t>(n_layers) * u_elems * sizeof(float)) +
-           align_up(static_cast<size_t>(n_layers) * st_elems * sizeof(float2)) +
-           align_up(static_cast<size_t>(n_layers) * lse_elems * sizeof(float2));
-  }
 };
+
+// The exchange kernel (chunk partials kept in LDS, per-row statistics
+// exchanged between the spans of a head inside one persistent launch) is
+// built and parity-tested but slower than the chunk-partial path on every
+// workload measured (its spans wait for the slowest span of their head each
+// round and pay several device-scope round trips), so it runs only when
+// CHUNKKV_SCORE_PATH=exchange asks for it.
+bool exchange_disabled() {
+  const char* v = std::getenv("CHUNKKV_SCORE_PATH");
+  return !(v && std::strcmp(v, "exchange") == 0);
+}
+
+// Polls of a head's ready flag before an exchange-mode span gives up and
+// spills its partials (CHUNKKV_SPIN_LIMIT overrides; 0 makes every span spill).
+int exchange_spin_limit() {
+  const char* v = std::getenv("CHUNKKV_SPIN_LIMIT");
+  if (!v || !*v) return 4096;
+  const long x = std::strtol(v, nullptr, 10);
+  return x < 0 ? 0 : (x > (1 << 24) ? (1 << 24) : static_cast<int>(x));
+}
 
 int make_plan(const chunkkv_problem* p, Plan& pl) {
   if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
@@ -124,6 +143,9 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   // per key token and head, written and read back) would outweigh a second
   // pass over the keys (2*d bytes)
   pl.two_pass = pl.mfma && pl.n_rb == 1 && score_two_pass_supported(pl.c);
+  pl.group_chunks = pl.mfma ? score_group_chunks(pl.c) : 0;
+  pl.x_max_span = pl.mfma && pl.n_rb == 1 && !pl.two_pass && !exchange_disabled()
+                      ? score_exchange_max_span_chunks(pl.c) : 0;
   pl.kv_st = p->kv_stride_tok;
   pl.kv_sh = p->kv_stride_head;
   pl.q_ss = p->q_stride_seq;
@@ -164,6 +186,132 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     return fail(CHUNKKV_ERR_UNSUPPORTED, "problem too large for one launch grid");
   pl.length_elems = static_cast<int64_t>(pl.B) * pl.Hkv;
   return CHUNKKV_OK;
+}
+
+// ------------------------------------------------------- exchange layout --
+
+// Resident exchange workgroups the span choice assumes (256 CUs x 3); the
+// launch packs its rounds with the device's own count.
+constexpr int kNominalSlots = 768;
+
+// Span layout of an exchange-mode score launch over nl layers: span length
+// (chunks), spans per head of each sequence, statistics offsets.
+struct XLayout {
+  bool ok = false;
+  int span_chunks = 0;
+  std::vector<int32_t> n_span;   // per sequence
+  std::vector<int64_t> st_off;   // per sequence: float2 offset of head 0, span 0 within a layer
+  int64_t st_elems = 0;          // float2 per layer
+  int64_t spill_elems = 0;       // spill flags per layer (one per span of every head)
+};
+
+// Rounds of one exchange launch (layers [0, nl), sequences [b0, b0 + nb)):
+// whole heads in flat item order (layer, sequence, head, span), at most
+// `slots` spans per round.  Returns the round count (0 if a head alone has
+// more spans than slots); fills round_start[0 .. rounds] (flat item indices,
+// the last one the end) when it is non-NULL and rounds <= kMaxRounds, and the
+// largest round's span count.
+int pack_rounds(const Plan& pl, const std::vector<int32_t>& n_span, int b0, int nb, int nl, int slots,
+                int32_t* round_start, int* max_round) {
+  int per_layer = 0;
+  for (int i = 0; i < nb; ++i) per_layer += pl.Hkv * n_span[b0 + i];
+  int rounds = 0, cur = 0, mx = 0, flat = 0;
+  for (int li = 0; li < nl; ++li)
+    for (int i = 0; i < nb; ++i)
+      for (int h = 0; h < pl.Hkv; ++h) {
+        const int ns = n_span[b0 + i];
+        if (ns > slots) return 0;
+        if (rounds == 0 || cur + ns > slots) {
+          mx = std::max(mx, cur);
+          if (round_start && rounds <= kMaxRounds) round_start[rounds] = flat;
+          ++rounds;
+          cur = 0;
+        }
+        cur += ns;
+        flat += ns;
+      }
+  mx = std::max(mx, cur);
+  if (round_start && rounds <= kMaxRounds) round_start[rounds] = nl * per_layer;
+  if (max_round) *max_round = mx;
+  return rounds;
+}
+
+// The span length (whole MFMA groups, at most the kernel's LDS ring allows)
+// that minimises the sum over launches of rounds x (groups per span + 1),
+// the +1 standing for a round's exchange; ties go to longer spans.  The
+// choice assumes kNominalSlots resident workgroups, so that workspace sizes
+// depend on the problem and the layer count alone.
+XLayout xlayout(const Plan& pl, int nl) {
+  XLayout xl;
+  if (pl.x_max_span <= 0 || pl.group_chunks <= 0 || nl < 1) return xl;
+  const int gmax = pl.x_max_span / pl.group_chunks;
+  int64_t best = -1;
+  int best_g = 0;
+  std::vector<int32_t> ns(pl.B);
+  for (int g = 1; g <= gmax; ++g) {
+    const int span = g * pl.group_chunks;
+    for (int b = 0; b < pl.B; ++b) ns[b] = (pl.seq[b].C + span - 1) / span;
+    int64_t cost = 0;
+    bool ok = true;
+    for (int b0 = 0; b0 < pl.B && ok; b0 += kMaxSeqs) {
+      const int r = pack_rounds(pl, ns, b0, std::min(kMaxSeqs, pl.B - b0), nl, kNominalSlots, nullptr, nullptr);
+      if (r < 1 || r > kMaxRounds) ok = false;
+      cost += static_cast<int64_t>(r) * (g + 1);
+    }
+    if (ok && (best < 0 || cost <= best)) {
+      best = cost;
+      best_g = g;
+    }
+  }
+  if (!best_g) return xl;
+  xl.ok = true;
+  xl.span_chunks = best_g * pl.group_chunks;
+  xl.n_span.resize(pl.B);
+  xl.st_off.resize(pl.B);
+  for (int b = 0; b < pl.B; ++b) {
+    xl.n_span[b] = (pl.seq[b].C + xl.span_chunks - 1) / xl.span_chunks;
+    xl.st_off[b] = xl.st_elems;
+    xl.st_elems += static_cast<int64_t>(pl.Hkv) * xl.n_span[b] * pl.R_pad;
+    xl.spill_elems += static_cast<int64_t>(pl.Hkv) * xl.n_span[b];
+  }
+  return xl;
+}
+
+// Workspace of nl scoring layers per launch: chunk partials U, span
+// statistics (sized for both span layouts), row statistics, then the
+// exchange launch's per-head words and per-span spill flags.
+struct Work {
+  float* U;
+  float2* st;
+  float2* lse;
+  uint32_t* sync;    // sync and spill are contiguous (one clearing launch)
+  uint32_t* spill;
+};
+
+size_t ws_need(const Plan& pl, int nl, const XLayout& xl) {
+  const int64_t st = std::max<int64_t>(pl.st_elems, xl.ok ? xl.st_elems : 0);
+  const int64_t flags = xl.ok ? static_cast<int64_t>(pl.B) * pl.Hkv * kSyncWords + xl.spill_elems : 0;
+  return align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float)) +
+         align_up(static_cast<size_t>(nl) * st * sizeof(float2)) +
+         align_up(static_cast<size_t>(nl) * pl.lse_elems * sizeof(float2)) +
+         align_up(static_cast<size_t>(nl) * flags * sizeof(uint32_t));
+}
+
+size_t ws_need(const Plan& pl, int nl) { return ws_need(pl, nl, xlayout(pl, nl)); }
+
+Work carve(const Plan& pl, int nl, const XLayout& xl, void* ws) {
+  const int64_t st = std::max<int64_t>(pl.st_elems, xl.ok ? xl.st_elems : 0);
+  const size_t u_bytes = align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float));
+  const size_t st_bytes = align_up(static_cast<size_t>(nl) * st * sizeof(float2));
+  const size_t lse_bytes = align_up(static_cast<size_t>(nl) * pl.lse_elems * sizeof(float2));
+  char* base = static_cast<char*>(ws);
+  Work w;
+  w.U = reinterpret_cast<float*>(base);
+  w.st = reinterpret_cast<float2*>(base + u_bytes);
+  w.lse = reinterpret_cast<float2*>(base + u_bytes + st_bytes);
+  w.sync = reinterpret_cast<uint32_t*>(base + u_bytes + st_bytes + lse_bytes);
+  w.spill = w.sync + static_cast<int64_t>(nl) * pl.B * pl.Hkv * kSyncWords;
+  return w;
 }
 
 // ------------------------------------------------------------- launchers --
@@ -320,19 +468,113 @@ int decode_rows_per_block(const Plan& pl) {
   return static_cast<int>(std::min<int64_t>(round_up(per, step), int64_t{1} << 30));
 }
 
-// Scores of nl scoring layers: chunk partials then the log-sum-exp combine,
-// or (pl.two_pass) statistics, row statistics and a final pass over the keys.
-hipError_t run_scores(const Plan& pl, int nl, const void* const* q, const void* const* k, float* U, float2* st,
-                      float2* lse, float* scores, hipStream_t s, hipEvent_t ev_start = nullptr,
+// Exchange-mode scores of nl scoring layers (one persistent launch per batch
+// of at most kMaxSeqs sequences, after one launch that clears the flags).
+// Returns hipErrorNotSupported, having launched nothing, when this device
+// cannot hold a round's spans at once or the launch would need more than
+// kMaxRounds rounds.
+hipError_t run_exchange(const Plan& pl, const XLayout& xl, int nl, const void* const* q, const void* const* k,
+                        const Work& w, float* scores, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  int slots = 0;
+  hipError_t e = score_exchange_slots(pl.c, &slots);
+  if (e != hipSuccess) return e;
+  if (slots < 8) return hipErrorNotSupported;
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int r = pack_rounds(pl, xl.n_span, b0, std::min(kMaxSeqs, pl.B - b0), nl, slots, nullptr, nullptr);
+    if (r < 1 || r > kMaxRounds) return hipErrorNotSupported;
+  }
+  // the per-head words of nl layers and the spill flags (which follow the
+  // per-head words of the workspace's layer count) in one clearing launch
+  const int64_t words = (w.spill - w.sync) + static_cast<int64_t>(nl) * xl.spill_elems;
+  if ((e = launch_zero_words(w.sync, words, s)) != hipSuccess) return e;
+  const int spin = exchange_spin_limit();
+  int64_t spans_before = 0;
+  for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
+    const int nb = std::min(kMaxSeqs, pl.B - b0);
+    ScoreParams P{};
+    for (int i = 0; i < nl; ++i) {
+      P.q[i] = q[i];
+      P.k[i] = k[i];
+    }
+    P.n_layers = nl;
+    P.n_seqs = nb;
+    P.span_chunks = xl.span_chunks;
+    int items = 0;
+    for (int i = 0; i < nb; ++i) {
+      const Seq& sq = pl.seq[b0 + i];
+      P.tok0[i] = sq.tok0;
+      P.qseq[i] = b0 + i;
+      P.T[i] = sq.T;
+      P.C[i] = sq.C;
+      P.n_span[i] = xl.n_span[b0 + i];
+      P.item0[i] = items;
+      P.u_off[i] = sq.u_off;
+      P.st_off[i] = xl.st_off[b0 + i];
+      P.s_off[i] = sq.score_off;
+      P.lse_off[i] = sq.lse_off;
+      items += pl.Hkv * xl.n_span[b0 + i];
+    }
+    P.item0[nb] = items;
+    P.items_per_layer = items;
+    P.u_layer_stride = pl.u_elems;
+    P.st_layer_stride = xl.st_elems;
+    P.s_layer_stride = pl.scores_elems;
+    P.lse_layer_stride = pl.lse_elems;
+    P.U = w.U;
+    P.stats = w.st;
+    P.lse_w = w.lse;
+    P.mode = kScoreExchange;
+    P.S = scores;
+    P.H_q = pl.Hq;
+    P.H_kv = pl.Hkv;
+    P.G = pl.G;
+    P.w = pl.w;
+    P.c = pl.c;
+    P.d = pl.d;
+    P.R = pl.R;
+    P.R_pad = pl.R_pad;
+    P.n_rb = pl.n_rb;
+    P.kv_st = pl.kv_st;
+    P.kv_sh = pl.kv_sh;
+    P.q_ss = pl.q_ss;
+    P.q_sr = pl.q_sr;
+    P.q_sh = pl.q_sh;
+    P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
+    P.rebase_raw = kRebaseLog2 / P.scale;
+    int max_round = 0;
+    P.n_rounds = pack_rounds(pl, xl.n_span, b0, nb, nl, slots, P.round_start, &max_round);
+    P.spin_limit = spin;
+    P.sync = w.sync + static_cast<int64_t>(nl) * b0 * pl.Hkv * kSyncWords;
+    P.spill = w.spill + static_cast<int64_t>(nl) * spans_before;
+    for (int i = 0; i < nb; ++i) spans_before += static_cast<int64_t>(pl.Hkv) * xl.n_span[b0 + i];
+    // persistent grid: the largest round, a multiple of 8 (positions are
+    // dealt XCD by XCD), at most the resident workgroups
+    const int grid = std::min(slots, (max_round + 7) / 8 * 8);
+    if ((e = launch_score_mfma(P, grid, s, ev_start, ev_stop)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Scores of nl scoring layers: the exchange kernel where it applies (xl.ok
+// and the device holds a round's spans), else chunk partials then the
+// log-sum-exp combine, or (pl.two_pass) statistics, row statistics and a
+// final pass over the keys.  ev_start / ev_stop: at the score kernel's own
+// start and end (one sequence batch, a single-launch score phase), or null.
+hipError_t run_scores(const Plan& pl, const XLayout& xl, int nl, const void* const* q, const void* const* k,
+                      const Work& w, float* scores, hipStream_t s, hipEvent_t ev_start = nullptr,
                       hipEvent_t ev_stop = nullptr) {
   hipError_t e;
-  if (!pl.two_pass) {
-    if ((e = run_score(pl, nl, q, k, U, st, s, ev_start, ev_stop)) != hipSuccess) return e;
-    return run_combine(pl, nl, U, st, lse, scores, s);
+  if (xl.ok) {
+    e = run_exchange(pl, xl, nl, q, k, w, scores, s, ev_start, ev_stop);
+    if (e != hipErrorNotSupported) return e;
   }
-  if ((e = run_score(pl, nl, q, k, U, st, s, nullptr, nullptr, kScoreStats)) != hipSuccess) return e;
-  if ((e = run_combine(pl, nl, U, st, lse, scores, s, true)) != hipSuccess) return e;
-  return run_score(pl, nl, q, k, U, st, s, nullptr, nullptr, kScoreFinal, lse, scores);
+  if (!pl.two_pass) {
+    if ((e = run_score(pl, nl, q, k, w.U, w.st, s, ev_start, ev_stop)) != hipSuccess) return e;
+    return run_combine(pl, nl, w.U, w.st, w.lse, scores, s);
+  }
+  if ((e = run_score(pl, nl, q, k, w.U, w.st, s, nullptr, nullptr, kScoreStats)) != hipSuccess) return e;
+  if ((e = run_combine(pl, nl, w.U, w.st, w.lse, scores, s, true)) != hipSuccess) return e;
+  return run_score(pl, nl, q, k, w.U, w.st, s, nullptr, nullptr, kScoreFinal, w.lse, scores);
 }
 
 hipError_t run_select(const Plan& pl, int nl, const float* scores, int32_t* indices, int32_t* lengths,
@@ -412,19 +654,11 @@ hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* 
   return hipSuccess;
 }
 
-void carve(const Plan& pl, int nl, void* ws, float** U, float2** st, float2** lse) {
-  const size_t u_bytes = align_up(static_cast<size_t>(nl) * pl.u_elems * sizeof(float));
-  const size_t st_bytes = align_up(static_cast<size_t>(nl) * pl.st_elems * sizeof(float2));
-  *U = static_cast<float*>(ws);
-  *st = reinterpret_cast<float2*>(static_cast<char*>(ws) + u_bytes);
-  *lse = reinterpret_cast<float2*>(static_cast<char*>(ws) + u_bytes + st_bytes);
-}
-
 int check_ws(const Plan& pl, const void* ws, size_t ws_bytes, int nl) {
   if (!ws) return fail(CHUNKKV_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign)
     return fail(CHUNKKV_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-  const size_t need = pl.ws_bytes(nl);
+  const size_t need = ws_need(pl, nl);
   if (ws_bytes < need)
     return fail(CHUNKKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return CHUNKKV_OK;
@@ -535,7 +769,7 @@ int chunkkv_plan(const chunkkv_problem* p, chunkkv_sizes* out, int64_t* score_of
   out->scores_elems = pl.scores_elems;
   out->index_elems = pl.index_elems;
   out->length_elems = pl.length_elems;
-  out->workspace_bytes = pl.ws_bytes(1);
+  out->workspace_bytes = ws_need(pl, 1);
   for (int b = 0; b < pl.B; ++b) {
     if (score_off) score_off[b] = pl.seq[b].score_off;
     if (index_off) index_off[b] = pl.seq[b].index_off;
@@ -547,7 +781,7 @@ int chunkkv_plan(const chunkkv_problem* p, chunkkv_sizes* out, int64_t* score_of
 size_t chunkkv_workspace_bytes(const chunkkv_problem* p, int32_t n_score_layers) {
   Plan pl;
   if (make_plan(p, pl) || n_score_layers < 1) return 0;
-  return pl.ws_bytes(std::min<int32_t>(n_score_layers, kMaxLayers));
+  return ws_need(pl, std::min<int32_t>(n_score_layers, kMaxLayers));
 }
 
 int chunkkv_score(const chunkkv_problem* p, const void* q_win, const void* k, float* scores, void* workspace,
@@ -560,10 +794,8 @@ int chunkkv_score(const chunkkv_problem* p, const void* q_win, const void* k, fl
     return fail(CHUNKKV_ERR_UNSUPPORTED, "q_win and k must be 16-byte aligned");
   if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* U;
-  float2 *st, *lse;
-  carve(pl, 1, workspace, &U, &st, &lse);
-  hipError_t e = run_scores(pl, 1, &q_win, &k, U, st, lse, scores, s);
+  const XLayout xl = xlayout(pl, 1);
+  hipError_t e = run_scores(pl, xl, 1, &q_win, &k, carve(pl, 1, xl, workspace), scores, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
   return ok();
 }
@@ -679,7 +911,8 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
   const int n_anchor = (n_layers + n_reuse - 1) / n_reuse;
   if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
   int batch = std::min(n_anchor, kMaxLayers);
-  while (batch > 1 && pl.ws_bytes(batch) > workspace_bytes) --batch;
+  while (batch > 1 && ws_need(pl, batch) > workspace_bytes) --batch;
+  const XLayout xl = xlayout(pl, batch);   // the last, shorter launch keeps this span layout
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) { return phase_events ? static_cast<hipEvent_t>(phase_events[i]) : nullptr; };
@@ -692,9 +925,7 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
   hipError_t e = score_events ? hipSuccess : record(0);
   if (e != hipSuccess) return hip_fail(e, "phase event");
 
-  float* U;
-  float2 *st, *lse;
-  carve(pl, batch, workspace, &U, &st, &lse);
+  const Work w = carve(pl, batch, xl, workspace);
   const void* qb[kMaxLayers];
   const void* kb[kMaxLayers];
   for (int a0 = 0; a0 < n_anchor; a0 += batch) {
@@ -704,17 +935,12 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
       kb[i] = k[(a0 + i) * n_reuse];
     }
     float* sc = scores + a0 * pl.scores_elems;
-    if (pl.two_pass) {
-      // statistics pass, row statistics and final pass: the score phase
-      if ((e = run_scores(pl, na, qb, kb, U, st, lse, sc, s)) != hipSuccess) return hip_fail(e, "score launch");
-      if (one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-    } else {
-      if ((e = score_events ? run_score(pl, na, qb, kb, U, st, s, ev(0), ev(1))
-                            : run_score(pl, na, qb, kb, U, st, s)) != hipSuccess)
-        return hip_fail(e, "score launch");
-      if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-      if ((e = run_combine(pl, na, U, st, lse, sc, s)) != hipSuccess) return hip_fail(e, "combine launch");
-    }
+    // the score phase: the exchange kernel, or chunk partials and their
+    // combine, or the two passes over the keys
+    if ((e = score_events ? run_scores(pl, xl, na, qb, kb, w, sc, s, ev(0), ev(1))
+                          : run_scores(pl, xl, na, qb, kb, w, sc, s)) != hipSuccess)
+      return hip_fail(e, "score launch");
+    if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
     if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
                         lengths + a0 * pl.length_elems, s)) != hipSuccess)
       return hip_fail(e, "select launch");

@@ -30,6 +30,9 @@ constexpr int kMfmaRows = 128;           // query rows (G*w) per MFMA score work
 #ifndef CKV_MIN_WAVES
 #define CKV_MIN_WAVES 2
 #endif
+#ifndef CKV_XCH_WAVES
+#define CKV_XCH_WAVES 3
+#endif
 constexpr int kGatherRows = CKV_GATHER_ROWS;   // output rows per gather workgroup
 constexpr int kSpanTarget = CKV_SPAN_TARGET;   // chunks per MFMA score work item (LDS-resident)
 constexpr int kMaxTiles = CKV_MAX_TILES;       // 32-slot MFMA tiles per group, at most
@@ -54,6 +57,18 @@ constexpr float kRebaseLog2 = 64.0f;
 constexpr int kScorePartials = 0;
 constexpr int kScoreStats = 1;
 constexpr int kScoreFinal = 2;
+// Mode kScoreExchange (one row block per head): the spans of a head run in
+// the same round of a persistent launch; each keeps its chunk partials in
+// LDS, publishes (m_ref, l) per row into stats, and the last span of the head
+// to arrive forms (M_r, L_r) into lse and raises the head's ready flag; every
+// span then writes its own chunk scores S from its LDS partials.  A span
+// whose wait for the flag runs out writes its partials to U instead (and
+// marks itself in spill); the last span of the head to finish scores the
+// marked spans from U with the same arithmetic.
+constexpr int kScoreExchange = 3;
+constexpr int kMaxRounds = 64;         // rounds of one exchange launch
+// Per-head words of an exchange launch: arrivals, finished spans, ready flag.
+constexpr int kSyncWords = 4;
 
 struct ScoreParams {
   const void* q[kMaxLayers];
@@ -92,6 +107,14 @@ struct ScoreParams {
   int64_t kv_st, kv_sh, q_ss, q_sr, q_sh;
   float scale;                  // log2(e) / sqrt(d)
   float rebase_raw;             // kRebaseLog2 / scale
+  // kScoreExchange: round r holds the items [round_start[r], round_start[r+1])
+  // (whole heads); the workgroup at position p takes item round_start[r] + p.
+  int32_t n_rounds;
+  int32_t round_start[kMaxRounds + 1];
+  int32_t spin_limit;           // polls of a head's ready flag before spilling
+  float2* lse_w;                // written (M_r, L_r), same layout as lse
+  uint32_t* sync;               // [n_layers][n_seqs * H_kv][kSyncWords], zero on entry
+  uint32_t* spill;              // [n_layers * items_per_layer], zero on entry
 };
 
 // --------------------------------------------------------------- combine --
@@ -193,6 +216,14 @@ inline hipError_t launch1(void (*kernel)(Arg), dim3 grid, dim3 block, size_t lds
 // ev_start / ev_stop (may be null) are recorded at the kernel's start and end.
 hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start = nullptr,
                              hipEvent_t ev_stop = nullptr);
+// Exchange mode: the largest span (in chunks) whose partials fit the
+// kernel's LDS ring for chunk size c (0: no exchange layout), the chunks per
+// MFMA group, and the persistent grid (resident workgroups, a multiple of 8).
+int score_exchange_max_span_chunks(int chunk);
+int score_group_chunks(int chunk);
+hipError_t score_exchange_slots(int chunk, int* slots);
+// Zeroes n 32-bit words (the exchange launch's flags) on stream s.
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s);
 // Generic path: any dtype / head_dim / chunk size (VALU fp32).
 int score_generic_span_chunks(int R_pad, int chunk);
 size_t score_generic_lds_bytes(int R_pad, int span_chunks, int d);

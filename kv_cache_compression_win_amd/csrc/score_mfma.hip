@@ -23,9 +23,11 @@
 // logit's final probability 2^((x - M_r)*scale - log2 L_r), sums it per chunk
 // in registers and over the block's 128 rows through LDS, and writes the
 // chunk scores themselves.
+#include <algorithm>
 #include <type_traits>
 
 #include "chunkkv_internal.h"
+#include "lse_combine.h"
 
 namespace ckv {
 namespace {
@@ -55,6 +57,10 @@ constexpr int kSharedKeySpans = 8;
 // outweigh a second read of the keys (2*d bytes).
 constexpr int kTwoPassMaxChunk = 3;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
+// LDS of an exchange-mode workgroup at most (three per 160 KB CU) and the
+// share of it kept for the launch tables.
+constexpr int kExchangeLdsBytes = 53 * 1024;
+constexpr int kTablesReserve = 1536;
 constexpr int kLdsAhead = 4;         // key fragment reads issued ahead of their MFMA
 constexpr int kPieces = kD / 8;      // 16-byte pieces per bf16 key row
 
@@ -91,6 +97,15 @@ struct Geo {
   static constexpr int LOADS = NT * 32 * kPieces / kThreads;  // uint4 per thread per group
   // register stages (groups of keys in flight), at least 2
   static constexpr int STAGES = (kStageTiles / NT) >= 2 ? (kStageTiles / NT > 4 ? 4 : kStageTiles / NT) : 2;
+  // Exchange mode: a ring of XSLOTS group slots of chunk partials in LDS,
+  // one more than the longest span (XGPS groups), so that the next span's
+  // first group has a free slot while the previous span still waits for its
+  // head's row statistics.  As many slots as keep three workgroups per CU.
+  static constexpr int KLDS_BYTES = NT * 32 * kPieces * 16;
+  static constexpr int SLOT_FLOATS = GROUP_CHUNKS * kMfmaRows;
+  static constexpr int XFIT = (kExchangeLdsBytes - KLDS_BYTES - kTablesReserve) / (SLOT_FLOATS * 4);
+  static constexpr int XSLOTS = XFIT < GPS + 1 ? XFIT : GPS + 1;
+  static constexpr int XGPS = XSLOTS >= 2 ? XSLOTS - 1 : 0;
 };
 
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
@@ -123,7 +138,8 @@ __device__ __forceinline__ float chunk_exp_sum(const f32x16 (&acc)[Geo<CC>::NT],
 template <int CC, bool STORE>
 __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool full, int nvalid,
                                               float scale, float rebase_raw, float& m_ref,
-                                              float& l_acc, float* u_row, int gi) {
+                                              float& l_acc, float* u_row, int gi, int base = 0,
+                                              int nslot = 1 << 20) {
   using G = Geo<CC>;
   if (!full) {
 #pragma unroll
@@ -152,16 +168,18 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
     if (mx > m_ref + rebase_raw) {
       const float f = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mx) * scale);
       if constexpr (STORE)
-        for (int gg = 0; gg < gi; ++gg)
+        for (int gg = 0; gg < gi; ++gg) {
+          const int sl = base + gg >= nslot ? base + gg - nslot : base + gg;
 #pragma unroll
-          for (int q = 0; q < G::CPH; ++q) u_row[(gg * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
+          for (int q = 0; q < G::CPH; ++q) u_row[(sl * G::GROUP_CHUNKS + q) * kMfmaRows] *= f;
+        }
       l_acc *= f;
       m_ref = mx;
 #pragma unroll
       for (int q = 0; q < G::CPH; ++q) u[q] = chunk_exp_sum<CC>(acc, q, scale, -m_ref * scale);
     }
   }
-  float* dst = u_row + gi * G::GROUP_CHUNKS * kMfmaRows;
+  float* dst = u_row + (base + gi >= nslot ? base + gi - nslot : base + gi) * G::GROUP_CHUNKS * kMfmaRows;
 #pragma unroll
   for (int q = 0; q < G::CPH; ++q) {
     if constexpr (STORE) dst[q * kMfmaRows] = u[q];
@@ -251,6 +269,7 @@ struct Tables {
   int32_t qseq[kMaxSeqs];
   int32_t wpu[kMaxSeqs];
   int32_t worker0[kMaxSeqs + 1];
+  int32_t round_start[kMaxRounds + 1];
 };
 
 __device__ __forceinline__ void load_tables(const ScoreParams& P, Tables& t) {
@@ -275,10 +294,12 @@ __device__ __forceinline__ void load_tables(const ScoreParams& P, Tables& t) {
     t.item0[i] = P.item0[i];
     t.worker0[i] = P.worker0[i];
   }
+  if (i <= kMaxRounds) t.round_start[i] = P.round_start[i];
 }
 
 template <int CC>
-__device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& t, int flat) {
+__device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& t, int flat,
+                                            int span_chunks = Geo<CC>::SPAN_CHUNKS) {
   using G = Geo<CC>;
   Item it;
   it.li = flat / P.items_per_layer;
@@ -293,8 +314,8 @@ __device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& 
   it.rb = hr % P.n_rb;
   it.h = hr / P.n_rb;
   it.C = sgpr(t.C[b]);
-  it.tok_begin = it.span * G::SPAN_CHUNKS * CC;
-  it.tok_end = min(sgpr(t.T[b]), it.tok_begin + G::SPAN_CHUNKS * CC);
+  it.tok_begin = it.span * span_chunks * CC;
+  it.tok_end = min(sgpr(t.T[b]), it.tok_begin + span_chunks * CC);
   it.ngroups = (it.tok_end - it.tok_begin + G::GROUP_TOK - 1) / G::GROUP_TOK;
   it.kbase = sgpr64(t.k[it.li]) +
              2 * static_cast<uint64_t>(static_cast<int64_t>(sgpr64(t.tok0[b])) * P.kv_st +
@@ -302,20 +323,124 @@ __device__ __forceinline__ Item decode_item(const ScoreParams& P, const Tables& 
   return it;
 }
 
-// Position in a workgroup's stream of key groups.
+// Position in a workgroup's stream of key groups: item `flat` (in round r
+// in exchange mode), group g of it.
 struct Cursor {
-  int flat, g;
+  int flat, g, r;
   Item it;
 };
 
-template <int CC>
-__device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& t, Cursor& c, int hi) {
+// Next round from r on (exclusive) in which the workgroup at position pos
+// has an item; n_rounds when there is none.
+__device__ __forceinline__ int next_round(const ScoreParams& P, const Tables& t, int r, int pos) {
+  ++r;
+  while (r < P.n_rounds && sgpr(t.round_start[r]) + pos >= sgpr(t.round_start[r + 1])) ++r;
+  return r;
+}
+
+template <int CC, int MODE>
+__device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& t, Cursor& c, int hi, int pos,
+                                            int span_chunks) {
   if (++c.g == c.it.ngroups) {
     c.g = 0;
-    if (++c.flat >= hi) return false;
-    c.it = decode_item<CC>(P, t, c.flat);
+    if constexpr (MODE == kScoreExchange) {
+      const int r = next_round(P, t, c.r, pos);
+      if (r >= P.n_rounds) return false;
+      c.r = r;
+      c.flat = sgpr(t.round_start[r]) + pos;
+    } else {
+      if (++c.flat >= hi) return false;
+    }
+    c.it = decode_item<CC>(P, t, c.flat, span_chunks);
   }
   return true;
+}
+
+// Exchange mode: the chunk scores of one span from its chunk partials (LDS
+// ring slots from `base`, or consecutive U rows in global memory) and the
+// per-row weights wts[r] = 2^((m_span,r - M_r) * scale) / L_r.  Eight teams
+// of 32 lanes take one chunk each per pass; lane l multiplies rows
+// 4l .. 4l+3 (one 16-byte read) and the team adds by a fixed butterfly, so
+// both sources give the same bits for the same partials.
+template <int CC, bool FROM_LDS>
+__device__ __forceinline__ void span_scores(const float* src, int base, const float* wts, int nch, float* S) {
+  using G = Geo<CC>;
+  const int tid = threadIdx.x, team = tid >> 5, l = tid & 31;
+  const float4 w4 = reinterpret_cast<const float4*>(wts)[l];
+  for (int q0 = 0; q0 < nch; q0 += kThreads / 32) {
+    const int q = q0 + team;
+    float acc = 0.0f;
+    if (q < nch) {
+      const float* row;
+      if constexpr (FROM_LDS) {
+        int sl = base + q / G::GROUP_CHUNKS;
+        if (sl >= G::XSLOTS) sl -= G::XSLOTS;
+        row = src + (sl * G::GROUP_CHUNKS + q % G::GROUP_CHUNKS) * kMfmaRows;
+      } else {
+        row = src + static_cast<int64_t>(q) * kMfmaRows;
+      }
+      const float4 u4 = reinterpret_cast<const float4*>(row)[l];
+      acc = fmaf(u4.x, w4.x, acc);
+      acc = fmaf(u4.y, w4.y, acc);
+      acc = fmaf(u4.z, w4.z, acc);
+      acc = fmaf(u4.w, w4.w, acc);
+    }
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (l == 0 && q < nch) S[q] = acc;
+  }
+}
+
+// Device-coherent accesses of the exchange (agent-scope relaxed atomics: on
+// gfx950 the stores write through the XCD's L2 and the loads read past it),
+// and the wait that orders this wave's earlier stores before its later
+// memory operations: compiler fences on both sides of an s_waitcnt on every
+// counter, so neither the compiler nor the hardware moves a store past it.
+// The common path of the exchange needs no L2-wide writeback or invalidate.
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+  const uint64_t v =
+      __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+__device__ __forceinline__ void store_coherent(float2* p, float2 x) {
+  const uint64_t v = static_cast<uint64_t>(__float_as_uint(x.x)) | (static_cast<uint64_t>(__float_as_uint(x.y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// rows_lse (same merge order and thread split) over the exchange's
+// device-coherent accesses: (M_r, L_r) of rows r < R from the head's n_span
+// published span statistics.
+__device__ __forceinline__ void rows_lse_coherent(const float2* st, int nspan, int R, int64_t R_pad, float scale,
+                                                  float2* lse) {
+  constexpr int kUnr = 16;
+  const int tpr = lse_tpr(R, kThreads);
+  const int sub = threadIdx.x % tpr;
+  for (int r = threadIdx.x / tpr; r < R; r += kThreads / tpr) {
+    float m = -INFINITY, l = 0.0f;
+    for (int s0 = sub; s0 < nspan; s0 += tpr * kUnr) {
+      float2 ml[kUnr];
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u) {
+        const int s = s0 + u * tpr;
+        ml[u] = s < nspan ? load_coherent(st + s * R_pad + r) : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u) lse_merge(m, l, ml[u].x, ml[u].y, scale);
+    }
+    for (int o = 1; o < tpr; o <<= 1) {
+      const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+      lse_merge(m, l, m2, l2, scale);
+    }
+    if (sub == 0) store_coherent(lse + r, make_float2(m, l));
+  }
 }
 
 // Each workgroup takes a balanced range of consecutive spans of ONE unit
@@ -325,22 +450,55 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 // groups k+1 .. k+STAGES-1 -- of this item or the next ones -- are in flight.
 // The ring is indexed statically (the loop is unrolled by STAGES), so each
 // LDS store waits only for the loads of its own stage.
+//
+// Exchange mode (kScoreExchange): the launch is persistent, one workgroup per
+// resident slot.  Round r holds whole heads; the workgroup at position p
+// (positions count the workgroups of XCD 0 first, then XCD 1, ..., so the
+// spans of a head share one XCD's L2) takes item round_start[r] + p, its
+// window-query fragments loaded per item during the previous item's last
+// group.  Chunk partials go to a ring of LDS slots instead of U.  At the end
+// of a span the workgroup publishes (m_ref, l) of its 128 rows and counts
+// itself in the head's arrivals; the last arrival forms the head's row
+// statistics (M_r, L_r) and raises the head's ready flag.  The span stays
+// pending (its slots untouched) while the next span starts; just before that
+// span would overwrite the pending slots (or at its own end), the workgroup
+// waits for the flag (a bounded number of polls), weights each row's partials
+// by 2^((m_ref - M_r) * scale) / L_r and writes the span's chunk scores.  If
+// the wait runs out (only when a head's spans are not all resident at once),
+// the partials go to U and the span is marked in spill; the last span of the
+// head to finish scores the marked spans from U.  Every flag and counter is
+// zero on entry (a separate launch clears them).
 template <int CC, int KAUX, int MODE>
-__global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(const ScoreParams P) {
+__global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : CKV_MIN_WAVES) void score_mfma_kernel(
+    const ScoreParams P) {
   using G = Geo<CC>;
+  constexpr bool XCH = MODE == kScoreExchange;
   constexpr int kLoadEvery = G::NT * kKSteps / G::LOADS;   // MFMAs per key load of the next group
   static_assert(kLoadEvery * G::LOADS == G::NT * kKSteps, "key loads must spread evenly over the MFMAs");
+  static_assert(!XCH || G::XGPS >= 1, "exchange mode needs at least two LDS group slots");
+  constexpr int kUFloats = XCH ? G::XSLOTS * G::SLOT_FLOATS : G::SPAN_CHUNKS * kMfmaRows;
   __shared__ u32x4 k_lds[G::NT * 32 * kPieces];
-  __shared__ float u_lds[G::SPAN_CHUNKS * kMfmaRows];
+  __shared__ float u_lds[kUFloats];
   __shared__ Tables tab;
+  __shared__ int x_word;   // exchange: a flag or counter value broadcast to the workgroup
+  static_assert(!XCH || sizeof(k_lds) + sizeof(u_lds) + sizeof(Tables) + 16 <= kExchangeLdsBytes,
+                "exchange-mode LDS must leave room for three workgroups per CU");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, ho = lane >> 5;
   load_tables(P, tab);
   __syncthreads();
-  int lo, hi;
-  {
+  const int span_chunks = XCH ? P.span_chunks : G::SPAN_CHUNKS;
+  int lo = 0, hi = 0, pos = 0, r0 = 0;
+  if constexpr (XCH) {
+    const int per_xcd = static_cast<int>(gridDim.x) / 8;
+    pos = (gridDim.x % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8)
+                               : static_cast<int>(blockIdx.x);
+    r0 = next_round(P, tab, -1, pos);
+    if (r0 >= P.n_rounds) return;
+    lo = sgpr(tab.round_start[r0]) + pos;
+  } else {
     const int li = blockIdx.x / P.workers_per_layer;
     const int wr = blockIdx.x - li * P.workers_per_layer;
     int b = 0;
@@ -358,8 +516,8 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     const int base = li * P.items_per_layer + tab.item0[b] + unit * ns;
     lo = base + piece * ns / wpu;
     hi = base + (piece + 1) * ns / wpu;
+    if (lo >= hi) return;
   }
-  if (lo >= hi) return;
 
   // window-query fragments (B operand) of this wave's 32 rows; rows >= R are zero
   bf16x8 bq[kKSteps];
@@ -409,6 +567,138 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
       k_lds[sr * kPieces + (p ^ (sr & 15))] = src[x];
     }
   };
+
+  // ---- exchange-mode addressing and steps ----
+  auto unit_sync = [&](const Item& it) {
+    return P.sync + (static_cast<int64_t>(it.li) * P.n_seqs * P.H_kv + it.b * P.H_kv + it.h) * kSyncWords;
+  };
+  auto unit_stats = [&](const Item& it) {   // span 0 of the head
+    return P.stats + it.li * P.st_layer_stride + sgpr64(tab.st_off[it.b]) +
+           static_cast<int64_t>(it.h) * it.nspan * P.R_pad;
+  };
+  auto unit_lse = [&](const Item& it) {
+    return P.lse_w + it.li * P.lse_layer_stride + sgpr64(tab.lse_off[it.b]) + static_cast<int64_t>(it.h) * P.R_pad;
+  };
+  auto unit_scores = [&](const Item& it) {  // chunk 0 of the head
+    return P.S + it.li * P.s_layer_stride + sgpr64(tab.s_off[it.b]) + static_cast<int64_t>(it.h) * it.C;
+  };
+  auto unit_u = [&](const Item& it) {       // chunk 0 of the head
+    return P.U + it.li * P.u_layer_stride + sgpr64(tab.u_off[it.b]) + static_cast<int64_t>(it.h) * it.C * P.R_pad;
+  };
+  int xbase = 0;               // ring slot of the current item's group 0
+  bool pend = false;           // a finished span waits for its head's row statistics
+  Item p_it{};
+  int p_flat = 0, p_base = 0;
+  float p_m = 0.0f;            // the pending span's reference m_ref of this lane's row
+  float* const wts = reinterpret_cast<float*>(k_lds);   // per-row weights (k_lds is free there)
+
+  // The pending span's chunk scores (or its partials to U), then its count in
+  // the head's finished spans; the last to finish scores the spilled spans.
+  auto finalize_pending = [&]() __attribute__((always_inline)) {
+    uint32_t* sy = unit_sync(p_it);
+    __syncthreads();   // every thread has read the last broadcast word
+    if (tid == 0) {
+      uint32_t v = load_coherent(sy + 2);
+      for (int spins = 0; v == 0 && spins < P.spin_limit; ++spins) {
+        __builtin_amdgcn_s_sleep(2);
+        v = load_coherent(sy + 2);
+      }
+      x_word = v != 0;
+    }
+    __syncthreads();
+    const bool ready = x_word != 0;
+    const int nch = min(span_chunks, p_it.C - p_it.span * span_chunks);
+    if (ready) {
+      if (ho == 0) {
+        const int r = wave * 32 + n;
+        float w = 0.0f;
+        if (r < P.R) {
+          w = span_weight(p_m, load_coherent(unit_lse(p_it) + r), P.scale);
+        }
+        wts[r] = w;
+      }
+      __syncthreads();
+      span_scores<CC, true>(u_lds, p_base, wts, nch, unit_scores(p_it) + p_it.span * span_chunks);
+    } else {
+      float* U = unit_u(p_it) + static_cast<int64_t>(p_it.span) * span_chunks * P.R_pad;
+      for (int e = tid; e < nch * (kMfmaRows / 4); e += kThreads) {
+        const int q = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
+        int sl = p_base + q / G::GROUP_CHUNKS;
+        if (sl >= G::XSLOTS) sl -= G::XSLOTS;
+        reinterpret_cast<float4*>(U + static_cast<int64_t>(q) * kMfmaRows)[c4] =
+            reinterpret_cast<const float4*>(u_lds + (sl * G::GROUP_CHUNKS + q % G::GROUP_CHUNKS) * kMfmaRows)[c4];
+      }
+      if (tid == 0) P.spill[p_flat] = 1u;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // finished spans count in the low 16 bits, spilled ones in the high bits
+      if (!ready) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t inc = ready ? 1u : 0x10001u;
+      x_word = static_cast<int>(__hip_atomic_fetch_add(sy + 1, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc);
+    }
+    __syncthreads();
+    if ((x_word & 0xffff) == p_it.nspan && (x_word >> 16) != 0) {
+      // every span of the head is scored or spilled and some spilled: score
+      // the spilled ones (their partials were released to U before their count)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const uint32_t* sp = P.spill + (p_flat - p_it.span);
+      const float2* st = unit_stats(p_it);
+      const float2* lse = unit_lse(p_it);
+      for (int sidx = 0; sidx < p_it.nspan; ++sidx) {
+        if (load_coherent(sp + sidx) == 0) continue;
+        if (tid < kMfmaRows) {
+          float w = 0.0f;
+          if (tid < P.R) w = span_weight(load_coherent(st + sidx * P.R_pad + tid).x, load_coherent(lse + tid), P.scale);
+          wts[tid] = w;
+        }
+        __syncthreads();
+        span_scores<CC, false>(unit_u(p_it) + static_cast<int64_t>(sidx) * span_chunks * P.R_pad, 0, wts,
+                               min(span_chunks, p_it.C - sidx * span_chunks),
+                               unit_scores(p_it) + sidx * span_chunks);
+        __syncthreads();
+      }
+    }
+    pend = false;
+  };
+
+  // End of an exchange-mode item: publish its row statistics, count it in
+  // its head's arrivals (the last arrival forms the row statistics and raises
+  // the ready flag), score the previous pending span if any, and leave this
+  // one pending.
+  auto publish = [&](const Item& it, float m_ref, float l_acc, int flat) __attribute__((always_inline)) {
+    const float l_row = l_acc + shfl_xor32(l_acc);
+    __syncthreads();   // every wave is past this group's fragment reads
+    float2* stage = reinterpret_cast<float2*>(k_lds);
+    if (ho == 0) stage[wave * 32 + n] = make_float2(m_ref, l_row);
+    __syncthreads();
+    uint32_t* sy = unit_sync(it);
+    if (wave == 0) {
+      float2* st = unit_stats(it) + it.span * P.R_pad;
+      store_coherent(st + lane, stage[lane]);
+      store_coherent(st + lane + 64, stage[lane + 64]);
+      wait_stores();
+      if (lane == 0) x_word = static_cast<int>(__hip_atomic_fetch_add(sy, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    __syncthreads();
+    if (x_word + 1 == it.nspan) {
+      // the last arrival: every span of the head has published
+      rows_lse_coherent(unit_stats(it), it.nspan, P.R, P.R_pad, P.scale, unit_lse(it));
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(sy + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (pend) finalize_pending();
+    pend = true;
+    p_it = it;
+    p_flat = flat;
+    p_base = xbase;
+    p_m = m_ref;
+    xbase += it.ngroups;
+    if (xbase >= G::XSLOTS) xbase -= G::XSLOTS;
+  };
+
   // Per-row span statistics and chunk partials of a finished item.  The
   // stores go through buffer resources sized to the data (pieces past the
   // span's last chunk are dropped), so their number is fixed: the compiler's
@@ -469,7 +759,7 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   };
 
   float* u_row = u_lds + ho * G::CPH * kMfmaRows + wave * 32 + n;
-  Cursor cc{lo, 0, decode_item<CC>(P, tab, lo)};   // group being computed
+  Cursor cc{lo, 0, r0, decode_item<CC>(P, tab, lo, span_chunks)};   // group being computed
   Cursor lc = cc;                             // next group to load
   // Every step issues exactly one group of loads: past the end of the range
   // the last group is loaded again (its data is never used), so the number of
@@ -478,7 +768,7 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   auto next_rsrc = [&]() {
     const __amdgpu_buffer_rsrc_t rsrc = group_rsrc(lc.it, lc.g);
     Cursor t = lc;
-    if (cursor_next<CC>(P, tab, t, hi)) lc = t;
+    if (cursor_next<CC, MODE>(P, tab, t, hi, pos, span_chunks)) lc = t;
     return rsrc;
   };
   auto load_next = [&](u32x4 (&dst)[G::LOADS]) {
@@ -507,10 +797,15 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
   }
   float m_ref = -INFINITY, l_acc = 0.0f;
 
-  // total key groups of this workgroup's range: the main loop is counted, so
+  // total key groups of this workgroup's items: the main loop is counted, so
   // its only branches are uniform ones around the compute and write-back
   int total = 0;
-  for (int f = lo; f < hi; ++f) total += decode_item<CC>(P, tab, f).ngroups;
+  if constexpr (XCH) {
+    for (int r = r0; r < P.n_rounds; r = next_round(P, tab, r, pos))
+      total += decode_item<CC>(P, tab, sgpr(tab.round_start[r]) + pos, span_chunks).ngroups;
+  } else {
+    for (int f = lo; f < hi; ++f) total += decode_item<CC>(P, tab, f).ngroups;
+  }
 
   // one group of the stream, held in ring stage S; steps past the end of the
   // range (live == false) still issue their loads (repeats of the last group)
@@ -549,20 +844,40 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
         if (mi + kLdsAhead < G::NT * kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       const Item& it = cc.it;
+      const bool last_group = cc.g + 1 == it.ngroups;
       const int gtok0 = it.tok_begin + cc.g * G::GROUP_TOK;
       const int nvalid = it.tok_end - (gtok0 + ho * G::HALF_TOK);
-      if constexpr (MODE == kScoreFinal)
+      if constexpr (MODE == kScoreFinal) {
         group_final<CC>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, nfin, red,
                         s_lds + wave * G::SPAN_CHUNKS + cc.g * G::GROUP_CHUNKS, lane, n, ho);
-      else
+      } else if constexpr (XCH) {
+        group_softmax<CC, true>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale, P.rebase_raw, m_ref,
+                                l_acc, u_row, cc.g, xbase, G::XSLOTS);
+      } else {
         group_softmax<CC, MODE == kScorePartials>(acc, gtok0 + G::GROUP_TOK <= it.tok_end, nvalid, P.scale,
                                                   P.rebase_raw, m_ref, l_acc, u_row, cc.g);
-      if (cc.g + 1 == it.ngroups) {
-        flush(it, m_ref, l_acc);
+      }
+      if (last_group) {
+        if constexpr (XCH) {
+          // the next item's window queries load while this one is published
+          Cursor t = cc;
+          if (cursor_next<CC, MODE>(P, tab, t, hi, pos, span_chunks)) load_q(t.it);
+          publish(it, m_ref, l_acc, cc.flat);
+        } else {
+          flush(it, m_ref, l_acc);
+        }
         m_ref = -INFINITY;
         l_acc = 0.0f;
       }
-      cursor_next<CC>(P, tab, cc, hi);
+      cursor_next<CC, MODE>(P, tab, cc, hi, pos, span_chunks);
+      if constexpr (XCH) {
+        // the next group would overwrite the pending span's first slot:
+        // score that span now (k_lds is free until the next store_group)
+        if (pend) {
+          const int sl = xbase + cc.g >= G::XSLOTS ? xbase + cc.g - G::XSLOTS : xbase + cc.g;
+          if (sl == p_base) finalize_pending();
+        }
+      }
     } else {
 #pragma unroll
       for (int x = 0; x < G::LOADS; ++x) regs[S][x] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[x], 0, KAUX);
@@ -580,6 +895,20 @@ __global__ __launch_bounds__(kThreads, CKV_MIN_WAVES) void score_mfma_kernel(con
     if constexpr (G::STAGES > 6) step(std::integral_constant<int, 6 % G::STAGES>{}, k0 + 6 < total);
     if constexpr (G::STAGES > 7) step(std::integral_constant<int, 7 % G::STAGES>{}, k0 + 7 < total);
   }
+  if constexpr (XCH) {
+    if (pend) finalize_pending();
+  }
+}
+
+struct ZeroArgs {
+  uint32_t* p;
+  int64_t n;
+};
+
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(const ZeroArgs a) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < a.n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    a.p[i] = 0u;
 }
 
 #define CKV_CHUNKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(15) X(16) X(20) X(25) X(30) X(32) X(40) X(64)
@@ -660,9 +989,73 @@ hipError_t launch_split(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev
                  ev_stop);
 }
 
+// Chunk sizes with an exchange-mode kernel: a static layout, not scored in
+// two passes, and at least two LDS group slots.
+// (Chunk sizes whose exchange kernel needs more than 168 VGPRs at three
+// waves per SIMD -- 12, 20, 30, 32, 40, 64 -- keep the chunk-partial path.)
+constexpr bool exchange_fits_registers(int c) {
+  return c == 4 || c == 5 || c == 6 || c == 8 || c == 10 || c == 15 || c == 16 || c == 25;
+}
+
+template <int CC>
+constexpr bool has_exchange() {
+  if constexpr (pick_tiles(CC) >= 1)
+    return CC > kTwoPassMaxChunk && Geo<CC>::XGPS >= 1 && exchange_fits_registers(CC);
+  else
+    return false;
+}
+
+template <int CC>
+int exchange_span_of() {
+  if constexpr (has_exchange<CC>())
+    return Geo<CC>::XGPS * Geo<CC>::GROUP_CHUNKS;
+  else
+    return 0;
+}
+
+template <int CC>
+int group_chunks_of() {
+  if constexpr (pick_tiles(CC) >= 1)
+    return Geo<CC>::GROUP_CHUNKS;
+  else
+    return 0;
+}
+
+template <int CC>
+hipError_t exchange_slots_of(int* slots) {
+  if constexpr (has_exchange<CC>()) {
+    static thread_local int cached_dev = -1, cached = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != cached_dev) {
+      int cus = 0, per_cu = 0;
+      if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+      if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<CC, kKeysOnce, kScoreExchange>,
+                                                            kThreads, 0)) != hipSuccess)
+        return e;
+      cached_dev = dev;
+      cached = cus * per_cu / 8 * 8;
+    }
+    *slots = cached;
+    return hipSuccess;
+  } else {
+    *slots = 0;
+    return hipSuccess;
+  }
+}
+
 template <int CC>
 hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if constexpr (pick_tiles(CC) >= 1) {
+    if (p.mode == kScoreExchange) {
+      // n_items is the persistent grid here (the largest round, a multiple of 8)
+      if constexpr (has_exchange<CC>())
+        return launch1(score_mfma_kernel<CC, kKeysOnce, kScoreExchange>, dim3(n_items), dim3(kThreads), 0, s, p, e0,
+                       e1);
+      else
+        return hipErrorInvalidValue;
+    }
     if (p.mode != kScorePartials) {
       // two passes: short chunks, one row block (keys read once per pass)
       if constexpr (CC <= kTwoPassMaxChunk) {
@@ -678,6 +1071,49 @@ hipError_t launch_if_laid_out(const ScoreParams& p, int n_items, hipStream_t s, 
   } else {
     return hipErrorInvalidValue;
   }
+}
+
+int score_exchange_max_span_chunks(int chunk) {
+  switch (chunk) {
+#define CKV_CASE(c) \
+  case c:           \
+    return exchange_span_of<c>();
+    CKV_CHUNKS(CKV_CASE)
+#undef CKV_CASE
+    default:
+      return 0;
+  }
+}
+
+int score_group_chunks(int chunk) {
+  switch (chunk) {
+#define CKV_CASE(c) \
+  case c:           \
+    return group_chunks_of<c>();
+    CKV_CHUNKS(CKV_CASE)
+#undef CKV_CASE
+    default:
+      return 0;
+  }
+}
+
+hipError_t score_exchange_slots(int chunk, int* slots) {
+  switch (chunk) {
+#define CKV_CASE(c) \
+  case c:           \
+    return exchange_slots_of<c>(slots);
+    CKV_CHUNKS(CKV_CASE)
+#undef CKV_CASE
+    default:
+      *slots = 0;
+      return hipSuccess;
+  }
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
+  return launch1(zero_words_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, ZeroArgs{p, n});
 }
 
 hipError_t launch_score_mfma(ScoreParams p, int n_items, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {

@@ -257,6 +257,50 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
 
 
+# ------------------------------------------- exchange mode and its fallback --
+# With CHUNKKV_SCORE_PATH=exchange (read by the library at every call), bf16
+# caches with head_dim 128, one 128-row block per head and a chunk size with
+# an exchange kernel are scored in one persistent launch whose spans exchange
+# per-row statistics (no chunk partials in memory); by default they take the
+# chunk-partial path (score kernel writing U, then the combine).
+# CHUNKKV_SPIN_LIMIT=0 makes every exchange span give up waiting for its
+# head's row statistics and spill its partials (the head's last span scores
+# them).
+
+@pytest.mark.parametrize("c", [4, 5, 6, 8, 10, 15, 16, 25])
+def test_exchange_spill_path_equals_normal_path(c, monkeypatch):
+    # two sequences, three scoring layers: every span spilled gives the same
+    # bits as every span scored from LDS (same products, same order)
+    monkeypatch.setenv("CHUNKKV_SCORE_PATH", "exchange")
+    case = random_case(ck.BF16, [3000, 1700], [300, 170], 32, 8, 128, 32, c, n_layers=3, n_reuse=1,
+                       seed=100 + c).run()
+    s_norm, i_norm, l_norm = case.scores.copy(), case.indices.copy(), case.lengths.copy()
+    _all_units(case)
+    monkeypatch.setenv("CHUNKKV_SPIN_LIMIT", "0")
+    case.run()
+    assert np.array_equal(case.scores.view(np.uint32), s_norm.view(np.uint32))
+    assert np.array_equal(case.indices, i_norm) and np.array_equal(case.lengths, l_norm)
+    _all_units(case)
+
+
+@pytest.mark.parametrize("seq_lens,l_max,n_layers", [([8192], [819], 1),             # the 8k layer's shape
+                                                      ([32768], [3276], 2),
+                                                      ([1000, 2500, 33, 640, 3000, 777, 1024, 50, 129],
+                                                       [100, 250, 5, 0, 300, 77, 1024, 49, 20], 2)])
+def test_exchange_path_matches_oracle(seq_lens, l_max, n_layers, monkeypatch):
+    # the exchange kernel on the 8k layer's shape, two 32k layers and nine
+    # ragged sequences (two launches); it agrees with the default
+    # chunk-partial path within tolerance
+    case = random_case(ck.BF16, seq_lens, l_max, 32, 8, 128, 32, 10, n_layers=n_layers, seed=len(seq_lens)).run()
+    _all_units(case)
+    s_part = case.scores.copy()
+    monkeypatch.setenv("CHUNKKV_SCORE_PATH", "exchange")
+    case.run()
+    err = np.abs(case.scores.astype(np.float64) - s_part)
+    assert np.all(err <= 2 * RTOL[ck.BF16] * np.abs(s_part.astype(np.float64)) + ATOL)
+    _all_units(case)
+
+
 def test_strided_kv_layout():
     # K/V with a padded head stride (d + 64 elements) and token stride.
     Hkv, d, T = 2, 128, 1100
