@@ -64,6 +64,7 @@ struct Plan {
   int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
   bool mfma = false;
   bool two_pass = false;   // statistics pass + final-score pass, no chunk partials
+  bool u_packed = false;   // chunk partials stored in 24 bits (bf16 problems)
   // exchange mode possible: its longest span (chunks) and the chunks per MFMA group
   int x_max_span = 0, group_chunks = 0;
   std::vector<Seq> seq;
@@ -146,6 +147,7 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   pl.group_chunks = pl.mfma ? score_group_chunks(pl.c) : 0;
   pl.x_max_span = pl.mfma && pl.n_rb == 1 && !pl.two_pass && !exchange_disabled()
                       ? score_exchange_max_span_chunks(pl.c) : 0;
+  pl.u_packed = pl.dtype == CHUNKKV_BF16;
   pl.kv_st = p->kv_stride_tok;
   pl.kv_sh = p->kv_stride_head;
   pl.q_ss = p->q_stride_seq;
@@ -176,7 +178,7 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     s.lse_off = pl.lse_elems;
     pl.scores_elems += static_cast<int64_t>(pl.Hkv) * s.C;
     pl.index_elems += static_cast<int64_t>(pl.Hkv) * s.L_cap;
-    if (!pl.two_pass) pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * pl.R_pad;
+    if (!pl.two_pass) pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * u_row_words(pl.R_pad, pl.u_packed);
     pl.st_elems += static_cast<int64_t>(pl.Hkv) * s.n_span * pl.R_pad;
     pl.lse_elems += static_cast<int64_t>(pl.Hkv) * pl.R_pad;
     items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * s.n_span;
@@ -355,6 +357,7 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
     P.s_layer_stride = pl.scores_elems;
     P.lse_layer_stride = pl.lse_elems;
     P.U = U;
+    P.u_packed = pl.u_packed ? 1 : 0;
     P.stats = st;
     P.mode = mode;
     P.S = scores;
@@ -430,6 +433,7 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
     P.score_layer_stride = pl.scores_elems;
     P.lse_layer_stride = pl.lse_elems;
     P.U = U;
+    P.u_packed = pl.u_packed ? 1 : 0;
     P.stats = st;
     P.lse = lse;
     P.scores = scores;
@@ -521,6 +525,7 @@ hipError_t run_exchange(const Plan& pl, const XLayout& xl, int nl, const void* c
     P.s_layer_stride = pl.scores_elems;
     P.lse_layer_stride = pl.lse_elems;
     P.U = w.U;
+    P.u_packed = 1;
     P.stats = w.st;
     P.lse_w = w.lse;
     P.mode = kScoreExchange;

@@ -43,11 +43,35 @@ constexpr int kStageTiles = CKV_STAGE_TILES;   // key tiles in flight per workgr
 // difference stays far inside fp32 range (2^64 * tokens << FLT_MAX).
 constexpr float kRebaseLog2 = 64.0f;
 
+// ------------------------------------------------- chunk-partial storage --
+// Chunk partials U (non-negative fp32) of bf16 problems are stored in 24
+// bits: the sign bit (always 0) dropped and the mantissa rounded to 16 bits
+// (relative error at most 2^-17, far inside the 1e-3 bound of bf16 inputs),
+// four values in three 32-bit words.  fp32 problems keep fp32 partials (their
+// bound is 1e-5).  A U row of R_pad values (R_pad a multiple of 4) takes
+// u_row_words(R_pad, packed) words; U offsets and strides count words.
+__host__ __device__ inline int64_t u_row_words(int64_t R_pad, bool packed) { return packed ? R_pad / 4 * 3 : R_pad; }
+
+typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
+// three words at a 4-byte aligned address of U (12-byte accesses)
+typedef unsigned int u32x3u __attribute__((ext_vector_type(3), aligned(4)));
+__device__ __forceinline__ uint32_t u24_of(float x) { return (__float_as_uint(x) + 0x40u) >> 7; }
+__device__ __forceinline__ float f_of_u24(uint32_t v) { return __uint_as_float(v << 7); }
+__device__ __forceinline__ float round_u24(float x) { return f_of_u24(u24_of(x)); }
+__device__ __forceinline__ u32x3v pack_u24(float a, float b, float c, float d) {
+  const uint32_t A = u24_of(a), B = u24_of(b), C = u24_of(c), D = u24_of(d);
+  return u32x3v{A | (B << 24), (B >> 8) | (C << 16), (C >> 16) | (D << 8)};
+}
+__device__ __forceinline__ float4 unpack_u24(u32x3v w) {
+  return make_float4(f_of_u24(w.x & 0xFFFFFFu), f_of_u24((w.x >> 24) | ((w.y & 0xFFFFu) << 8)),
+                     f_of_u24((w.y >> 16) | ((w.z & 0xFFu) << 16)), f_of_u24(w.z >> 8));
+}
+
 // ----------------------------------------------------------------- score --
 // One launch scores up to kMaxLayers layers x kMaxSeqs sequences.  Work item
 // = (layer, sequence b, KV head h, row block rb, span s); a span is a run of
 // span_chunks whole chunks.  In mode kScorePartials each item writes
-//   U[layer][u_off[b] + (h*C_b + j)*R_pad + r]      chunk partials
+//   U[layer][u_off[b] + (h*C_b + j)*u_row_words + row r]  chunk partials
 //   stats[layer][st_off[b] + (h*n_span_b + s)*R_pad + r] = (m_ref, l)
 // where U is sum over the chunk's tokens of exp2((x - m_ref)*scale) and l
 // is sum over the span of the same terms.  Short chunks (two passes over the
@@ -91,11 +115,12 @@ struct ScoreParams {
   int32_t C[kMaxSeqs];
   int32_t n_span[kMaxSeqs];
   int32_t item0[kMaxSeqs + 1];  // first item of sequence b within a layer
-  int64_t u_off[kMaxSeqs];
+  int64_t u_off[kMaxSeqs];       // U offsets and strides in 32-bit words
   int64_t st_off[kMaxSeqs];
   int64_t u_layer_stride;
   int64_t st_layer_stride;
-  float* U;
+  float* U;                     // 32-bit words: packed 24-bit partials when u_packed
+  int32_t u_packed;
   float2* stats;
   int32_t mode;                 // kScorePartials, kScoreStats or kScoreFinal
   float* S;                     // kScoreFinal: chunk scores
@@ -138,8 +163,9 @@ struct CombineParams {
   int64_t lse_off[kMaxSeqs];    // per-row (M, L) of sequence b: [H_kv][R_pad] float2
   int32_t head0[kMaxSeqs + 1];  // first (sequence, head) item of sequence b in the row-statistics launch
   int32_t fuse_lse;             // 1: each combine block forms its head's (M_r, L_r) itself (no row-statistics launch)
-  int64_t u_layer_stride, st_layer_stride, score_layer_stride, lse_layer_stride;
-  const float* U;
+  int64_t u_layer_stride, st_layer_stride, score_layer_stride, lse_layer_stride;   // U: 32-bit words
+  const float* U;               // packed 24-bit partials when u_packed
+  int32_t u_packed;
   const float2* stats;
   float2* lse;
   float* scores;

@@ -26,7 +26,7 @@ namespace {
 constexpr int kMaxRows = 4096;
 constexpr int kWeightFloats = 16384;  // weights of one item's spans (64 KB at most)
 
-template <int QPT>
+template <int QPT, bool PACKED>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P) {
   // dynamic LDS: weights [spans_per_blk][R_pad], then (fuse_lse) the row
   // statistics [R_pad] as float2
@@ -70,11 +70,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams P
   }
   __syncthreads();
 
-  const float* U = P.U + li * P.u_layer_stride + P.u_off[b] + static_cast<int64_t>(h) * C * P.R_pad;
+  const float* U = P.U + li * P.u_layer_stride + P.u_off[b] + static_cast<int64_t>(h) * C * u_row_words(P.R_pad, PACKED);
   float* S = P.scores + li * P.score_layer_stride + P.score_off[b] + static_cast<int64_t>(h) * C;
   const int j_lo = s_lo * P.span_chunks;
   const int j_hi = min(C, (s_lo + ns) * P.span_chunks);
-  combine_chunks<kThreads, QPT>(U, wts, j_lo, j_hi, s_lo, P.span_chunks, P.R_pad, S);
+  combine_chunks<kThreads, QPT, PACKED>(U, wts, j_lo, j_hi, s_lo, P.span_chunks, P.R_pad, S);
 }
 
 // Row statistics of one (layer, sequence, KV head): (M_r, L_r) over all spans,
@@ -108,14 +108,19 @@ hipError_t launch_combine(const CombineParams& p, int n_blocks, hipStream_t s) {
   if (p.R_pad > kMaxRows || p.spans_per_blk * p.R_pad > kWeightFloats) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(p.spans_per_blk) * p.R_pad * sizeof(float) +
                     (p.fuse_lse ? static_cast<size_t>(p.R_pad) * sizeof(float2) : 0);
+#define CKV_COMBINE(Q)                                                                                   \
+  case Q:                                                                                                \
+    return p.u_packed ? launch1(combine_kernel<Q, true>, dim3(n_blocks), dim3(kThreads), lds, s, p)    \
+                      : launch1(combine_kernel<Q, false>, dim3(n_blocks), dim3(kThreads), lds, s, p);
   switch (combine_qpt(p.R_pad)) {
-    case 1: return launch1(combine_kernel<1>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-    case 2: return launch1(combine_kernel<2>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-    case 4: return launch1(combine_kernel<4>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-    case 8: return launch1(combine_kernel<8>, dim3(n_blocks), dim3(kThreads), lds, s, p);
-    case 16: return launch1(combine_kernel<16>, dim3(n_blocks), dim3(kThreads), lds, s, p);
+    CKV_COMBINE(1)
+    CKV_COMBINE(2)
+    CKV_COMBINE(4)
+    CKV_COMBINE(8)
+    CKV_COMBINE(16)
     default: return hipErrorInvalidValue;
   }
+#undef CKV_COMBINE
 }
 
 }  // namespace ckv

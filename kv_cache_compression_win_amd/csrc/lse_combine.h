@@ -84,13 +84,14 @@ __host__ __device__ inline int combine_qpt(int R_pad) {
 
 // Chunk scores S[j] = sum_r U[j][r] * wts[j / span_chunks - s_lo][r] for the
 // chunks j in [j_lo, j_hi) of one (layer, sequence, head): U rows are
-// R_pad floats (padding rows carry weight 0), wts holds R_pad weights per
-// span starting at span s_lo.  Groups of tpc consecutive threads share a
-// chunk; thread `sub` sums its float4 row quads q = sub + k*tpc (k < QPT) in
-// order, then a fixed butterfly over the group, so the result depends on
-// neither the workgroup size nor the unrolling.  All loads of an iteration
-// (8 float4 per thread) are issued before any arithmetic.
-template <int NTHREADS, int QPT>
+// u_row_words(R_pad, PACKED) words (padding rows carry weight 0), wts holds
+// R_pad weights per span starting at span s_lo.  Groups of tpc consecutive
+// threads share a chunk; thread `sub` sums its row quads q = sub + k*tpc
+// (k < QPT, 16 bytes of fp32 or 12 bytes of packed partials each) in order,
+// then a fixed butterfly over the group, so the result depends on neither
+// the workgroup size nor the unrolling.  All loads of an iteration (8 quads
+// per thread) are issued before any arithmetic.
+template <int NTHREADS, int QPT, bool PACKED>
 __device__ __forceinline__ void combine_chunks(const float* U, const float* wts, int j_lo, int j_hi,
                                                int s_lo, int span_chunks, int R_pad, float* S) {
   constexpr int kUnr = QPT >= 8 ? 1 : 8 / QPT;
@@ -98,16 +99,24 @@ __device__ __forceinline__ void combine_chunks(const float* U, const float* wts,
   const int groups = NTHREADS / tpc;
   const int g = threadIdx.x / tpc, sub = threadIdx.x % tpc;
   const int q4 = R_pad / 4;
+  const int64_t row_words = u_row_words(R_pad, PACKED);
   for (int j0 = j_lo; j0 < j_hi; j0 += groups * kUnr) {
     float4 a[kUnr][QPT];
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
       const int j = j0 + u * groups + g;
-      const float4* up = reinterpret_cast<const float4*>(U + static_cast<int64_t>(j) * R_pad);
+      const float* row = U + static_cast<int64_t>(j) * row_words;
 #pragma unroll
       for (int k = 0; k < QPT; ++k) {
         const int q = sub + k * tpc;
-        a[u][k] = (j < j_hi && q < q4) ? up[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (j < j_hi && q < q4) {
+          if constexpr (PACKED)
+            a[u][k] = unpack_u24(*reinterpret_cast<const u32x3u*>(row + 3 * q));
+          else
+            a[u][k] = reinterpret_cast<const float4*>(row)[q];
+        } else {
+          a[u][k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
       }
     }
 #pragma unroll

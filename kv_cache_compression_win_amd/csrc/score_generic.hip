@@ -114,8 +114,19 @@ __global__ __launch_bounds__(kThreads) void score_generic_kernel(const ScorePara
     wave_sync();
   }
   __syncthreads();
-  float* ug = P.U + li * P.u_layer_stride + P.u_off[b] + (static_cast<int64_t>(h) * C + chunk0) * P.R_pad;
-  for (int e = tid; e < nch * P.R_pad; e += kThreads) ug[e] = u_lds[e];
+  const int64_t row_words = u_row_words(P.R_pad, P.u_packed != 0);
+  float* ug = P.U + li * P.u_layer_stride + P.u_off[b] + (static_cast<int64_t>(h) * C + chunk0) * row_words;
+  if (P.u_packed) {
+    // 24-bit partials: 4 rows in 3 words
+    const int q4 = P.R_pad / 4;
+    for (int e = tid; e < nch * q4; e += kThreads) {
+      const int j = e / q4, q = e - j * q4;
+      const float4 v = *reinterpret_cast<const float4*>(u_lds + j * P.R_pad + 4 * q);
+      *reinterpret_cast<u32x3u*>(ug + j * row_words + 3 * q) = pack_u24(v.x, v.y, v.z, v.w);
+    }
+  } else {
+    for (int e = tid; e < nch * P.R_pad; e += kThreads) ug[e] = u_lds[e];
+  }
 }
 
 }  // namespace

@@ -357,11 +357,11 @@ __device__ __forceinline__ bool cursor_next(const ScoreParams& P, const Tables& 
 }
 
 // Exchange mode: the chunk scores of one span from its chunk partials (LDS
-// ring slots from `base`, or consecutive U rows in global memory) and the
-// per-row weights wts[r] = 2^((m_span,r - M_r) * scale) / L_r.  Eight teams
-// of 32 lanes take one chunk each per pass; lane l multiplies rows
-// 4l .. 4l+3 (one 16-byte read) and the team adds by a fixed butterfly, so
-// both sources give the same bits for the same partials.
+// ring slots from `base`, or consecutive packed U rows in global memory) and
+// the per-row weights wts[r] = 2^((m_span,r - M_r) * scale) / L_r.  Eight
+// teams of 32 lanes take one chunk each per pass; lane l multiplies rows
+// 4l .. 4l+3 and the team adds by a fixed butterfly.  Partials read from LDS
+// are rounded to the 24 bits U stores, so both sources give the same bits.
 template <int CC, bool FROM_LDS>
 __device__ __forceinline__ void span_scores(const float* src, int base, const float* wts, int nch, float* S) {
   using G = Geo<CC>;
@@ -371,15 +371,15 @@ __device__ __forceinline__ void span_scores(const float* src, int base, const fl
     const int q = q0 + team;
     float acc = 0.0f;
     if (q < nch) {
-      const float* row;
+      float4 u4;
       if constexpr (FROM_LDS) {
         int sl = base + q / G::GROUP_CHUNKS;
         if (sl >= G::XSLOTS) sl -= G::XSLOTS;
-        row = src + (sl * G::GROUP_CHUNKS + q % G::GROUP_CHUNKS) * kMfmaRows;
+        u4 = reinterpret_cast<const float4*>(src + (sl * G::GROUP_CHUNKS + q % G::GROUP_CHUNKS) * kMfmaRows)[l];
+        u4 = make_float4(round_u24(u4.x), round_u24(u4.y), round_u24(u4.z), round_u24(u4.w));
       } else {
-        row = src + static_cast<int64_t>(q) * kMfmaRows;
+        u4 = unpack_u24(*reinterpret_cast<const u32x3u*>(src + static_cast<int64_t>(q) * (kMfmaRows / 4 * 3) + 3 * l));
       }
-      const float4 u4 = reinterpret_cast<const float4*>(row)[l];
       acc = fmaf(u4.x, w4.x, acc);
       acc = fmaf(u4.y, w4.y, acc);
       acc = fmaf(u4.z, w4.z, acc);
@@ -582,8 +582,9 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
   auto unit_scores = [&](const Item& it) {  // chunk 0 of the head
     return P.S + it.li * P.s_layer_stride + sgpr64(tab.s_off[it.b]) + static_cast<int64_t>(it.h) * it.C;
   };
-  auto unit_u = [&](const Item& it) {       // chunk 0 of the head
-    return P.U + it.li * P.u_layer_stride + sgpr64(tab.u_off[it.b]) + static_cast<int64_t>(it.h) * it.C * P.R_pad;
+  auto unit_u = [&](const Item& it) {       // chunk 0 of the head (32-bit words, packed partials)
+    return P.U + it.li * P.u_layer_stride + sgpr64(tab.u_off[it.b]) +
+           static_cast<int64_t>(it.h) * it.C * u_row_words(kMfmaRows, true);
   };
   int xbase = 0;               // ring slot of the current item's group 0
   bool pend = false;           // a finished span waits for its head's row statistics
@@ -620,13 +621,15 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
       __syncthreads();
       span_scores<CC, true>(u_lds, p_base, wts, nch, unit_scores(p_it) + p_it.span * span_chunks);
     } else {
-      float* U = unit_u(p_it) + static_cast<int64_t>(p_it.span) * span_chunks * P.R_pad;
+      constexpr int kRowWords = kMfmaRows / 4 * 3;
+      float* U = unit_u(p_it) + static_cast<int64_t>(p_it.span) * span_chunks * kRowWords;
       for (int e = tid; e < nch * (kMfmaRows / 4); e += kThreads) {
         const int q = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
         int sl = p_base + q / G::GROUP_CHUNKS;
         if (sl >= G::XSLOTS) sl -= G::XSLOTS;
-        reinterpret_cast<float4*>(U + static_cast<int64_t>(q) * kMfmaRows)[c4] =
+        const float4 v =
             reinterpret_cast<const float4*>(u_lds + (sl * G::GROUP_CHUNKS + q % G::GROUP_CHUNKS) * kMfmaRows)[c4];
+        *reinterpret_cast<u32x3u*>(U + static_cast<int64_t>(q) * kRowWords + 3 * c4) = pack_u24(v.x, v.y, v.z, v.w);
       }
       if (tid == 0) P.spill[p_flat] = 1u;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -654,7 +657,7 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
           wts[tid] = w;
         }
         __syncthreads();
-        span_scores<CC, false>(unit_u(p_it) + static_cast<int64_t>(sidx) * span_chunks * P.R_pad, 0, wts,
+        span_scores<CC, false>(unit_u(p_it) + static_cast<int64_t>(sidx) * span_chunks * (kMfmaRows / 4 * 3), 0, wts,
                                min(span_chunks, p_it.C - sidx * span_chunks),
                                unit_scores(p_it) + sidx * span_chunks);
         __syncthreads();
@@ -739,13 +742,15 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
                                           (wave * 32 + n) * 8 + ho * kMfmaRows * 8, 0, 0);
     if constexpr (MODE == kScoreStats) return;
     __syncthreads();
+    // packed 24-bit partials (bf16 problems): 12 bytes per 4 rows
     const int nch = sgpr(min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS));
+    const int64_t row_words = u_row_words(P.R_pad, true);
     const uint64_t ubase = reinterpret_cast<uint64_t>(P.U + it.li * P.u_layer_stride) +
                            4 * static_cast<uint64_t>(sgpr64(tab.u_off[it.b]) +
                                                      (static_cast<int64_t>(it.h) * it.C + it.span * G::SPAN_CHUNKS) *
-                                                         P.R_pad +
-                                                     it.rb * kMfmaRows);
-    const int chunk_bytes = P.R_pad * 4;
+                                                         row_words +
+                                                     u_row_words(it.rb * kMfmaRows, true));
+    const int chunk_bytes = static_cast<int>(row_words * 4);
     const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>(sgpr64(ubase)), 0, nch * chunk_bytes, kBufferWord3);
     constexpr int kPieces4 = G::SPAN_CHUNKS * (kMfmaRows / 4);
@@ -753,8 +758,8 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
     for (int x = 0; x < (kPieces4 + kThreads - 1) / kThreads; ++x) {
       const int e = x * kThreads + tid;
       const int j = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
-      const u32x4 val = reinterpret_cast<const u32x4*>(u_lds)[min(e, kPieces4 - 1)];
-      __builtin_amdgcn_raw_buffer_store_b128(val, ru, j * chunk_bytes + c4 * 16, 0, 0);
+      const float4 val = reinterpret_cast<const float4*>(u_lds)[min(e, kPieces4 - 1)];
+      __builtin_amdgcn_raw_buffer_store_b96(pack_u24(val.x, val.y, val.z, val.w), ru, j * chunk_bytes + c4 * 12, 0, 0);
     }
   };
 
