@@ -19,6 +19,7 @@ import argparse
 import concurrent.futures
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -73,8 +74,11 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--context", choices=("on", "off"), default="on",
                     help="after the timed steps, also time the 8-layer slice and a 1 GiB device copy")
-    ap.add_argument("--cpu-anchor-pairs", type=int, default=2,
-                    help="oracle sample: this many (scoring, reusing) layer pairs, all KV heads")
+    ap.add_argument("--cpu-anchor-pairs", type=int, default=0,
+                    help="oracle sample: this many (scoring, reusing) layer pairs, all KV heads "
+                         "(0: every layer of the workload)")
+    ap.add_argument("--context-70b", choices=("on", "off"), default="on",
+                    help="after everything else, also time the 70B-shaped 80-layer batch (about 107 GB of HBM)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -264,32 +268,49 @@ def selection_overlap(bufs, wl, n_reuse, plan):
             "pairs": f"scoring layers l and l + {n_reuse}, sequence 0, all {H} KV heads"}
 
 
+# Host multiply-adds per second of one oracle thread (the fp64 score loop),
+# used only to bound the default CPU sample.
+ORACLE_MACS_PER_THREAD = 4.0e8
+CPU_BUDGET_S = 60.0
+
+
 def cpu_baseline(wl, cache, n_pairs: int):
-    """Time the CPU oracle, as it stands, on a bounded sample: the first
-    n_pairs (anchor layer, reusing layer) pairs of sequence 0, every KV head,
-    each unit running Algorithm 1 on the anchor and the gather on both."""
+    """Time the CPU oracle, as it stands, on the workload's own inputs copied
+    to the host: for every (scoring layer, KV head) of sequence 0, Algorithm 1
+    (fp64 scores, full-sort top-k, index build) on the scoring layer and the
+    row copies of K and V of that layer and of the layers reusing its indices.
+    n_pairs > 0 takes only the first n_pairs scoring layers; n_pairs = 0 takes
+    every layer of the workload when its estimated cost fits CPU_BUDGET_S of
+    wall time, else the largest leading sample that does (labelled)."""
     import oracle
     import kvsynth
     oracle.build(force=False)
     T = wl.seq_lens[0]
-    layers = [l for p in range(n_pairs) for l in (p * wl.n_reuse, p * wl.n_reuse + 1)
-              if l < wl.n_layers]
+    n_anchor = -(-wl.n_layers // wl.n_reuse)
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    rows = wl.window * (wl.n_q_heads // wl.n_kv_heads)
+    unit_s = rows * T * wl.head_dim / ORACLE_MACS_PER_THREAD
+    fit = max(1, int(CPU_BUDGET_S * threads / (unit_s * wl.n_kv_heads)))
+    pairs = min(n_anchor, n_pairs if n_pairs > 0 else fit)
+    whole = pairs == n_anchor and len(wl.seq_lens) == 1
+    groups = {a * wl.n_reuse: [l for l in range(a * wl.n_reuse, min((a + 1) * wl.n_reuse, wl.n_layers))]
+              for a in range(pairs)}
+    layers = [l for g in groups.values() for l in g]
     host = {l: (kvsynth.host_array(cache["k"][l, :T]), kvsynth.host_array(cache["v"][l, :T]))
             for l in layers}
-    qh = {l: kvsynth.host_array(cache["q_win"][l, 0]) for l in layers if l % wl.n_reuse == 0}
+    qh = {a: kvsynth.host_array(cache["q_win"][a, 0]) for a in groups}
     kk = wl.l_max[0] // wl.chunk
 
     def unit(args):
         a, h = args
         s = oracle.chunk_scores(qh[a], host[a][0], h, wl.n_q_heads, wl.window, wl.chunk)
         idx = oracle.indices(T, wl.window, wl.chunk, oracle.topk(s, kk))
-        for l in (a, a + 1):
-            if l in host:
-                oracle.gather(host[l][0], idx, h)
-                oracle.gather(host[l][1], idx, h)
+        for l in groups[a]:
+            oracle.gather(host[l][0], idx, h)
+            oracle.gather(host[l][1], idx, h)
 
-    jobs = [(a, h) for a in sorted(qh) for h in range(wl.n_kv_heads)]
-    threads = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    jobs = [(a, h) for a in sorted(groups) for h in range(wl.n_kv_heads)]
+    threads = max(1, min(len(jobs), threads))
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(unit, jobs))
@@ -307,13 +328,118 @@ def cpu_baseline(wl, cache, n_pairs: int):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
+    what = ("the whole workload" if whole else
+            f"a sample: layers {layers[0]}-{layers[-1]} of {wl.n_layers}, sequence 0 only")
     return {"value": layer_tokens / dt, "unit": "layer-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"layers {layers} of sequence 0 (T={T}), all {wl.n_kv_heads} KV heads: "
-                       f"fp64 scoring + full-sort top-k + index build on the scoring layers, "
-                       f"row copies on all; {dt:.2f} s wall"),
+            "sample": (f"{what} (T={T}, {len(layers)} layers, all {wl.n_kv_heads} KV heads): "
+                       f"fp64 scoring + full-sort top-k + index build on the {len(groups)} scoring layers, "
+                       f"row copies on all {len(layers)}; {dt:.2f} s wall on {threads} threads"),
             "single_thread": {"value": layer_tokens * n1 / len(jobs) / dt1, "unit": "layer-tokens/s",
-                              "sample": f"{n1} of the {len(jobs)} (layer pair, KV head) units, {dt1:.2f} s"},
+                              "sample": f"{n1} of the {len(jobs)} (scoring layer, KV head) units, {dt1:.2f} s"},
             "host": {"cpu_model": model, "logical_cpus": os.cpu_count()}}
+
+
+def layer_latency_context(name, args, start, stop, chunk=None, l_max=None, calls=40, blocks=5):
+    """A single-layer compress_layers call (score, select and gather of one
+    layer): median and minimum over blocks of back-to-back calls."""
+    import torch
+    import kvsynth
+    from kv_cache_compression_win_amd import chunkkv as ck
+    wl = kvsynth.WORKLOADS[name]
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    c = chunk or wl.chunk
+    lm = l_max or wl.l_max
+    prob = ck.make_problem(ck.BF16, wl.seq_lens, lm, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, c)
+    bufs = ck.Buffers(prob, 1, 1, wl.head_dim, torch.bfloat16, "cuda")
+
+    def call():
+        ck.compress_layers(prob, 1, [cache["q_win"][0]], [cache["k"][0]], [cache["v"][0]], [bufs.k_out[0]],
+                           [bufs.v_out[0]], bufs.scores, bufs.indices, bufs.lengths, bufs.workspace, bufs.ws_bytes)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    us = []
+    for _ in range(blocks):
+        start.record()
+        for _ in range(calls):
+            call()
+        stop.record()
+        torch.cuda.synchronize()
+        us.append(start.elapsed_time(stop) / calls * 1e3)
+    return {"workload": name, "chunk": c, "l_max": list(lm), "us_per_call_median": statistics.median(us),
+            "us_per_call_min": min(us), "blocks": blocks, "calls_per_block": calls}
+
+
+def context_70b(args):
+    """The 70B-shaped batch (80 layers, 64 query heads, 8 KV heads, four
+    packed sequences of 131072 / 65536 / 32768 / 16384 tokens, 20% budget,
+    index reuse 2), inputs resident in HBM: 5 timed steps of the whole stack
+    (median, minimum and mean step), and the score kernel alone on the first
+    64 layers (32 scoring layers: one score launch, its own start and end
+    events) against the dense bf16 MFMA peak and the HBM peak."""
+    import torch
+    import kvsynth
+    from kv_cache_compression_win_amd import accounting
+    from kv_cache_compression_win_amd import chunkkv as ck
+    wl = kvsynth.WORKLOADS["llama-70b-80layer-4seq"]
+    cache = kvsynth.make_cache(wl, device="cuda", seed=0)
+    L, nr, e = wl.n_layers, wl.n_reuse, 2
+    prob = ck.make_problem(ck.BF16, wl.seq_lens, wl.l_max, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window,
+                           wl.chunk)
+    bufs = ck.Buffers(prob, L, nr, wl.head_dim, torch.bfloat16, "cuda")
+    qs = [cache["q_win"][l] if l % nr == 0 else None for l in range(L)]
+    ks = [cache["k"][l] for l in range(L)]
+    vs = [cache["v"][l] for l in range(L)]
+    kos = [bufs.k_out[l] for l in range(L)]
+    vos = [bufs.v_out[l] for l in range(L)]
+
+    def step(n, events=None):
+        ck.compress_layers(prob, nr, qs[:n], ks[:n], vs[:n], kos[:n], vos[:n], bufs.scores, bufs.indices,
+                           bufs.lengths, bufs.workspace, bufs.ws_bytes, phase_events=events)
+
+    for _ in range(2):
+        step(L)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    evs[0].record()
+    for i in range(5):
+        step(L)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
+    mean_ms = evs[0].elapsed_time(evs[5]) / 5
+    n_anchor = -(-L // nr)
+    kept = bufs.lengths.view(n_anchor, -1).sum(dim=1).tolist()
+    step_bytes = (n_anchor * accounting.score_bytes(wl.seq_lens, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                    wl.window, wl.chunk, e)
+                  + sum(accounting.select_bytes(wl.seq_lens, wl.n_kv_heads, wl.chunk, k) for k in kept)
+                  + accounting.gather_bytes(sum(kept[l // nr] for l in range(L)), wl.head_dim, e))
+    # the score kernel of the first 32 scoring layers (one launch)
+    n64 = 64
+    sev = [ck.PhaseEvents() for _ in range(3)]
+    for ev in sev:
+        step(n64, ev)
+    torch.cuda.synchronize()
+    score_ms = statistics.median(ev.elapsed_ms(0, 1) for ev in sev)
+    a64 = n64 // nr
+    flops = a64 * 2 * wl.window * wl.n_q_heads * wl.head_dim * sum(wl.seq_lens)
+    kbytes = a64 * (sum(wl.seq_lens) * wl.n_kv_heads * wl.head_dim * e
+                    + len(wl.seq_lens) * wl.window * wl.n_q_heads * wl.head_dim * e)
+    tflops = flops / (score_ms * 1e-3) / 1e12
+    gbps = kbytes / (score_ms * 1e-3) / 1e9
+    out = {"workload": wl.name, "steps": 5, "ms_per_step_mean": mean_ms, "ms_per_step_median": statistics.median(ms),
+           "ms_per_step_min": min(ms), "value": L * sum(wl.seq_lens) / (mean_ms * 1e-3), "unit": "layer-tokens/s",
+           "step_hbm": {"achieved": step_bytes / (mean_ms * 1e-3) / 1e9,
+                        "frac": step_bytes / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": step_bytes},
+           "score_kernel": {"layers": "first 64 layers: 32 scoring layers in one score launch", "ms": score_ms,
+                            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": flops},
+                            "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes": kbytes}}}
+    del cache, bufs
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -370,15 +496,24 @@ def main():
     evs = [ck.PhaseEvents() for _ in range(args.steps)]
     score_only = [[e.handles[0], e.handles[1], None, None] for e in evs]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps fall into at least 3 blocks (as many as steps allow, at
+    # most 4), each bracketed by stream events, for a median and a minimum
+    n_blocks = min(args.steps, max(3, min(4, args.steps)))
+    bounds = [round(i * args.steps / n_blocks) for i in range(n_blocks + 1)]
+    block_evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
+        if i in bounds:
+            block_evs[bounds.index(i)].record()
         step(score_only[i])
+    block_evs[n_blocks].record()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
+    block_ms = [block_evs[j].elapsed_time(block_evs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(n_blocks)]
 
     def mean_ms(i, j):
         return sum(e.elapsed_ms(i, j) for e in evs) / len(evs)
@@ -427,6 +562,11 @@ def main():
         "step_hbm": {"achieved": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "algorithmic_bytes": step_bytes},
         "phases_ms": ph,
+        "timing": {"blocks": n_blocks, "steps_per_block": [bounds[j + 1] - bounds[j] for j in range(n_blocks)],
+                   "ms_per_step_blocks": block_ms, "ms_per_step_median": statistics.median(block_ms),
+                   "ms_per_step_min": min(block_ms),
+                   "what": "the timed steps in consecutive blocks, stream events between steps; value uses the "
+                           "mean over all timed steps"},
         "wall_s_timed": wall,
     }
     # context outside the timed region: the 8-layer slice (its first 8
@@ -481,9 +621,20 @@ def main():
     if n_copy:
         extra["copy_peak"] = copy_peak(n_copy, start, stop, step_gbps)
     out.update(extra)
+    if args.context == "on":
+        # single-layer calls: bound by launch and latency more than by bytes
+        extra_l = {"llama3-8b-1layer-T8192": layer_latency_context("llama3-8b-1layer-T8192", args, start, stop),
+                   "llama3-8b-csweep-T16384 (c = 10, L_max = 512)":
+                       layer_latency_context("llama3-8b-csweep-T16384", args, start, stop, chunk=10, l_max=(512,))}
+        out["single_layer_calls"] = extra_l
     if args.cpu_baseline == "on":
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, cache, args.cpu_anchor_pairs)
+    if args.context == "on" and args.context_70b == "on" and wl.name != "llama-70b-80layer-4seq":
+        print("[bench] the 70B-shaped batch (context)", file=sys.stderr, flush=True)
+        del cache, bufs, qs, ks, vs, kos, vos
+        torch.cuda.empty_cache()
+        out["llama_70b_80layer_4seq"] = context_70b(args)
     print(json.dumps(out), flush=True)
 
 

@@ -68,9 +68,16 @@ __device__ __forceinline__ float span_weight(float m_span, float2 lse, float sca
 
 // Threads that share one chunk's dot product: R_pad/4 row quads, at most a
 // wave (a power of two dividing 64).
+#ifndef CKV_COMBINE_TPC
+#define CKV_COMBINE_TPC 8
+#endif
+#ifndef CKV_COMBINE_INFLIGHT
+#define CKV_COMBINE_INFLIGHT 8
+#endif
 __host__ __device__ inline int combine_tpc(int R_pad) {
   int t = 1;
-  while (t < 64 && t < R_pad / 4) t <<= 1;
+  while (t < CKV_COMBINE_TPC && t < R_pad / 4) t <<= 1;
+  while (t < 64 && (R_pad / 4 + t - 1) / t > 16) t <<= 1;   // at most 16 row quads per thread
   return t;
 }
 
@@ -94,7 +101,7 @@ __host__ __device__ inline int combine_qpt(int R_pad) {
 template <int NTHREADS, int QPT, bool PACKED>
 __device__ __forceinline__ void combine_chunks(const float* U, const float* wts, int j_lo, int j_hi,
                                                int s_lo, int span_chunks, int R_pad, float* S) {
-  constexpr int kUnr = QPT >= 8 ? 1 : 8 / QPT;
+  constexpr int kUnr = QPT >= CKV_COMBINE_INFLIGHT ? 1 : CKV_COMBINE_INFLIGHT / QPT;
   const int tpc = combine_tpc(R_pad);
   const int groups = NTHREADS / tpc;
   const int g = threadIdx.x / tpc, sub = threadIdx.x % tpc;
