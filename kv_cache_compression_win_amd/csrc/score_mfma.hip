@@ -489,7 +489,9 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
   const int n = lane & 31, ho = lane >> 5;
   load_tables(P, tab);
   __syncthreads();
-  const int span_chunks = XCH ? P.span_chunks : G::SPAN_CHUNKS;
+  // chunks per span: the host's choice (whole groups, at most SPAN_CHUNKS);
+  // the two-pass final mode keeps SPAN_CHUNKS (its LDS row sums are laid out for it)
+  const int span_chunks = MODE == kScoreFinal ? G::SPAN_CHUNKS : P.span_chunks;
   int lo = 0, hi = 0, pos = 0, r0 = 0;
   if constexpr (XCH) {
     const int per_xcd = static_cast<int>(gridDim.x) / 8;
@@ -743,11 +745,11 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
     if constexpr (MODE == kScoreStats) return;
     __syncthreads();
     // packed 24-bit partials (bf16 problems): 12 bytes per 4 rows
-    const int nch = sgpr(min(G::SPAN_CHUNKS, it.C - it.span * G::SPAN_CHUNKS));
+    const int nch = sgpr(min(span_chunks, it.C - it.span * span_chunks));
     const int64_t row_words = u_row_words(P.R_pad, true);
     const uint64_t ubase = reinterpret_cast<uint64_t>(P.U + it.li * P.u_layer_stride) +
                            4 * static_cast<uint64_t>(sgpr64(tab.u_off[it.b]) +
-                                                     (static_cast<int64_t>(it.h) * it.C + it.span * G::SPAN_CHUNKS) *
+                                                     (static_cast<int64_t>(it.h) * it.C + it.span * span_chunks) *
                                                          row_words +
                                                      u_row_words(it.rb * kMfmaRows, true));
     const int chunk_bytes = static_cast<int>(row_words * 4);
@@ -809,7 +811,7 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
     for (int r = r0; r < P.n_rounds; r = next_round(P, tab, r, pos))
       total += decode_item<CC>(P, tab, sgpr(tab.round_start[r]) + pos, span_chunks).ngroups;
   } else {
-    for (int f = lo; f < hi; ++f) total += decode_item<CC>(P, tab, f).ngroups;
+    for (int f = lo; f < hi; ++f) total += decode_item<CC>(P, tab, f, span_chunks).ngroups;
   }
 
   // one group of the stream, held in ring stage S; steps past the end of the
