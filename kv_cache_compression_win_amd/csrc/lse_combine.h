@@ -68,16 +68,17 @@ __device__ __forceinline__ float span_weight(float m_span, float2 lse, float sca
 
 // Threads that share one chunk's dot product: R_pad/4 row quads, at most a
 // wave (a power of two dividing 64).
-#ifndef CKV_COMBINE_TPC
-#define CKV_COMBINE_TPC 8
+#ifndef CKV_COMBINE_QUADS
+#define CKV_COMBINE_QUADS 4
 #endif
 #ifndef CKV_COMBINE_INFLIGHT
 #define CKV_COMBINE_INFLIGHT 8
 #endif
+// Threads sharing a chunk: each takes about CKV_COMBINE_QUADS row quads (8
+// threads for 128 rows, 32 for 512), a power of two of at most a wave.
 __host__ __device__ inline int combine_tpc(int R_pad) {
   int t = 1;
-  while (t < CKV_COMBINE_TPC && t < R_pad / 4) t <<= 1;
-  while (t < 64 && (R_pad / 4 + t - 1) / t > 16) t <<= 1;   // at most 16 row quads per thread
+  while (t < 64 && t * CKV_COMBINE_QUADS < R_pad / 4) t <<= 1;
   return t;
 }
 

@@ -48,7 +48,13 @@ constexpr int kBufferWord3 = 0x00020000;
 // displace the chunk partials and window queries in L2.  With several row
 // blocks (G*w > 128) the blocks of a head read the same keys on one XCD at
 // about the same time: ordinary caching lets that XCD's L2 serve the repeats.
-constexpr int kKeysOnce = 2;
+#ifndef CKV_KEYS_AUX
+#define CKV_KEYS_AUX 2
+#endif
+#ifndef CKV_U_STORE_AUX
+#define CKV_U_STORE_AUX 0
+#endif
+constexpr int kKeysOnce = CKV_KEYS_AUX;
 constexpr int kKeysShared = 0;
 constexpr int kSharedKeySpans = 8;
 // Chunk sizes scored in two passes over the keys (statistics, then final
@@ -761,7 +767,8 @@ __global__ __launch_bounds__(kThreads, MODE == kScoreExchange ? CKV_XCH_WAVES : 
       const int e = x * kThreads + tid;
       const int j = e / (kMfmaRows / 4), c4 = e % (kMfmaRows / 4);
       const float4 val = reinterpret_cast<const float4*>(u_lds)[min(e, kPieces4 - 1)];
-      __builtin_amdgcn_raw_buffer_store_b96(pack_u24(val.x, val.y, val.z, val.w), ru, j * chunk_bytes + c4 * 12, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b96(pack_u24(val.x, val.y, val.z, val.w), ru, j * chunk_bytes + c4 * 12, 0,
+                                            CKV_U_STORE_AUX);
     }
   };
 
