@@ -507,6 +507,54 @@ def test_select_any_scores_stays_in_range(T, c, w, l_max):
                 assert np.array_equal(idx, oracle.indices(T, w, c, sel))
 
 
+def _digit_scores(rng, C, kind):
+    """Scores whose bit patterns share their top 8, 16 or 24 bits (the select
+    must resolve the k-th largest in a later radix digit), tie in large groups,
+    or are all distinct; fp32 patterns of non-negative values."""
+    if kind == "distinct":
+        return rng.random(C).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(0, 5, C).astype(np.float32) / 4.0
+    shared = {"share8": 8, "share16": 16, "share24": 24}[kind]
+    base = np.uint32(0x3f000000)
+    low = rng.integers(0, 1 << (31 - shared), C, dtype=np.uint64).astype(np.uint32)
+    bits = (base & np.uint32(~((1 << (31 - shared)) - 1) & 0x7fffffff)) | low
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("C", [1, 63, 64, 65, 512, 513, 1025, 4096, 4097, 8193])
+@pytest.mark.parametrize("kind", ["distinct", "ties", "share8", "share16", "share24"])
+def test_select_threshold_bits(C, kind):
+    # chunkkv_select against the oracle's full-sort top-k on score sets whose
+    # k-th largest differs from its neighbours only in the low 23, 15 or 7
+    # bits of its pattern (the bitwise threshold search must run through all
+    # of them), tie at the k-th score, or sit on either side of the register
+    # layouts' chunk limits (1, 2, 8 and 16 scores per thread of 512);
+    # budgets from one chunk to all but one.
+    c, w = 4, 3
+    T = C * c - 1 if C > 1 else 3
+    Hkv = 2
+    rng = np.random.default_rng(C * 31 + len(kind))
+    for kk in sorted({1, max(1, C // 3), max(1, C - 1)}):
+        prob = ck.make_problem(ck.F32, [T], [kk * c], 4, Hkv, 64, w, c)
+        pl = ck.plan(prob)
+        host = np.concatenate([_digit_scores(rng, C, kind) for _ in range(Hkv)])
+        scores = torch.from_numpy(host).cuda()
+        indices = torch.full((pl["index_elems"],), POISON_INDEX, dtype=torch.int32, device="cuda")
+        lengths = torch.zeros(Hkv, dtype=torch.int32, device="cuda")
+        ck.select(prob, scores, indices, lengths)
+        torch.cuda.synchronize()
+        idx_all, n_all = indices.cpu().numpy(), lengths.cpu().numpy()
+        L_cap = int(pl["l_cap"][0])
+        for h in range(Hkv):
+            s = host[h * C:(h + 1) * C].astype(np.float64)
+            want = oracle.indices(T, w, c, oracle.topk(s, min(kk, C)))
+            n = int(n_all[h])
+            assert n == len(want) <= L_cap, (kind, C, kk, h)
+            assert np.array_equal(idx_all[h * L_cap:h * L_cap + n], want), (kind, C, kk, h)
+            assert np.all(idx_all[h * L_cap + n:(h + 1) * L_cap] == POISON_INDEX)
+
+
 def test_gather_clamps_caller_indices_and_lengths():
     # chunkkv_gather with caller-made indices and lengths: lengths are
     # clamped into [0, L_cap] and index values into [0, T); rows past the
