@@ -236,6 +236,66 @@ int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t 
                             size_t workspace_bytes, void *stream, void *const *phase_events);
 
 /*
+ * The hybrid layer policy (ChunkKV page, section 5.7: chunk-level selection in
+ * some layers, token-level selection, i.e. c = 1, in others) as a per-layer
+ * chunk size.  layer_chunk is a HOST [n_layers] table of chunk sizes; p->chunk
+ * is ignored and every other field of p applies to all layers.  Layers are
+ * taken in runs of consecutive layers with the same chunk size, and Algorithm
+ * 2 (section 4.2) restarts at each run: in a run starting at layer r0, layer
+ * l scores iff (l - r0) mod n_reuse == 0 and otherwise gathers with the
+ * indices of anchor r0 + floor((l - r0) / n_reuse) * n_reuse, so indices are
+ * never reused across a change of chunk size.
+ *
+ * Host-only planning of chunkkv_compress_layers_hybrid's buffers.  Anchors
+ * are numbered in layer order; anchor a's scores, indices and lengths start at
+ * element score_block_off[a], index_block_off[a] and length_block_off[a] of
+ * the scores, indices and lengths buffers, each block laid out as
+ * chunkkv_sizes describes for the problem with that anchor's chunk size;
+ * entry n_anchor of each array holds the buffer's total size in elements.
+ * kv_out_rows[l] is the row count of layer l's K'/V' (the index_elems of its
+ * chunk size).  workspace_bytes is the largest chunkkv_workspace_bytes(p_c, 1)
+ * over the chunk sizes c used.
+ *   n_anchor          HOST out, may be NULL
+ *   *_block_off       HOST int64 [n_layers + 1] out (n_anchor <= n_layers),
+ *                     each may be NULL
+ *   kv_out_rows       HOST int64 [n_layers] out, may be NULL
+ *   workspace_bytes   HOST out, may be NULL
+ * Errors: INVALID_ARG (layer_chunk NULL, n_layers < 1, n_reuse < 1, or a
+ * layer's problem invalid, as in chunkkv_plan), UNSUPPORTED.
+ */
+int chunkkv_plan_hybrid(const chunkkv_problem *p, const int32_t *layer_chunk, int32_t n_layers,
+                        int32_t n_reuse, int32_t *n_anchor, int64_t *score_block_off,
+                        int64_t *index_block_off, int64_t *length_block_off, int64_t *kv_out_rows,
+                        size_t *workspace_bytes);
+
+/*
+ * chunkkv_compress_layers with a per-layer chunk size (the layer runs and
+ * block layout of chunkkv_plan_hybrid): the scoring layers of every run are
+ * scored and selected, then every layer is gathered.  Arguments as in
+ * chunkkv_compress_layers, with
+ *   scores, indices, lengths  DEVICE, the anchors' blocks at the offsets
+ *                   chunkkv_plan_hybrid gives (totals in its entry n_anchor)
+ *   k_out[l], v_out[l]  DEVICE, kv_out_rows[l] rows each
+ *   workspace       DEVICE scratch of >= chunkkv_plan_hybrid's
+ *                   workspace_bytes bytes
+ *   phase_events    NULL, or HOST [CHUNKKV_N_PHASE_EVENTS] hipEvent_t
+ *                   handles recorded on `stream` before the first scoring
+ *                   launch, after the last selection (entries 1 and 2) and
+ *                   after the last gather.
+ * The call allocates nothing and issues only kernel launches (and the phase
+ * events).  Its outputs equal those of one chunkkv_compress_layers call per
+ * run with that run's chunk size.
+ * Errors: as chunkkv_plan_hybrid, and as chunkkv_compress_layers.
+ */
+int chunkkv_compress_layers_hybrid(const chunkkv_problem *p, const int32_t *layer_chunk,
+                                   int32_t n_layers, int32_t n_reuse, const void *const *q_win,
+                                   const void *const *k, const void *const *v,
+                                   void *const *k_out, void *const *v_out, float *scores,
+                                   int32_t *indices, int32_t *lengths, void *workspace,
+                                   size_t workspace_bytes, void *stream,
+                                   void *const *phase_events);
+
+/*
  * Workspace needed by chunkkv_decode_attention for problem p: per-block
  * partials of every (sequence, KV head, block of kept rows, query head).
  * Host only.  Returns 0 on invalid input.

@@ -23,7 +23,7 @@ N_PHASE_EVENTS = 4
 SYMBOLS = ("chunkkv_plan", "chunkkv_workspace_bytes", "chunkkv_score", "chunkkv_select",
            "chunkkv_gather", "chunkkv_compress_layers", "chunkkv_decode_workspace_bytes",
            "chunkkv_decode_attention", "chunkkv_decode_attention_static", "chunkkv_gather_paged",
-           "chunkkv_last_error")
+           "chunkkv_plan_hybrid", "chunkkv_compress_layers_hybrid", "chunkkv_last_error")
 STATIC_SCRATCH_BYTES = 16 << 20
 
 
@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.chunkkv_decode_attention_static.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.chunkkv_gather_paged.restype = ctypes.c_int
         L.chunkkv_gather_paged.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp]
+        L.chunkkv_plan_hybrid.restype = ctypes.c_int
+        L.chunkkv_plan_hybrid.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.chunkkv_compress_layers_hybrid.restype = ctypes.c_int
+        L.chunkkv_compress_layers_hybrid.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                     vp, vp]
         L.chunkkv_last_error.restype = ctypes.c_char_p
         L.chunkkv_last_error.argtypes = []
         _lib = L
@@ -286,6 +291,64 @@ def compress_layers(prob, n_reuse: int, q_win: Sequence, k: Sequence, v: Sequenc
         ctypes.cast(vot, ctypes.c_void_p), _ptr(scores), _ptr(indices), _ptr(lengths),
         _ptr(workspace), workspace_nbytes, _stream(stream),
         None if ev is None else ctypes.cast(ev, ctypes.c_void_p)))
+
+
+def plan_hybrid(prob, layer_chunk: Sequence[int], n_reuse: int) -> dict:
+    """chunkkv_plan_hybrid: per-anchor block offsets (with the totals as the
+    last entry), each layer's K'/V' row count and the workspace size."""
+    n = len(layer_chunk)
+    ch = (ctypes.c_int32 * n)(*layer_chunk)
+    na = ctypes.c_int32(0)
+    so, io, lo = (ctypes.c_int64 * (n + 1))(), (ctypes.c_int64 * (n + 1))(), (ctypes.c_int64 * (n + 1))()
+    rows = (ctypes.c_int64 * n)()
+    ws = ctypes.c_size_t(0)
+    _check(lib().chunkkv_plan_hybrid(prob.ref, ctypes.cast(ch, ctypes.c_void_p), n, n_reuse, ctypes.byref(na),
+                                     ctypes.cast(so, ctypes.c_void_p), ctypes.cast(io, ctypes.c_void_p),
+                                     ctypes.cast(lo, ctypes.c_void_p), ctypes.cast(rows, ctypes.c_void_p),
+                                     ctypes.byref(ws)))
+    a = na.value
+    return {"n_anchor": a, "score_block_off": list(so[:a + 1]), "index_block_off": list(io[:a + 1]),
+            "length_block_off": list(lo[:a + 1]), "kv_out_rows": list(rows), "workspace_bytes": ws.value}
+
+
+def compress_layers_hybrid(prob, layer_chunk: Sequence[int], n_reuse: int, q_win: Sequence, k: Sequence,
+                           v: Sequence, k_out: Sequence, v_out: Sequence, scores, indices, lengths, workspace,
+                           workspace_nbytes: int, stream=None, phase_events: Optional[Sequence] = None) -> None:
+    n = len(k)
+    if len(layer_chunk) != n:
+        raise ValueError("layer_chunk needs one chunk size per layer")
+    ch = (ctypes.c_int32 * n)(*layer_chunk)
+    P = ctypes.c_void_p * n
+    qt = P(*[_ptr(x) for x in q_win])
+    kt, vt = P(*[_ptr(x) for x in k]), P(*[_ptr(x) for x in v])
+    kot, vot = P(*[_ptr(x) for x in k_out]), P(*[_ptr(x) for x in v_out])
+    ev = None
+    if phase_events is not None:
+        hs = phase_events.handles if isinstance(phase_events, PhaseEvents) else list(phase_events)
+        ev = (ctypes.c_void_p * N_PHASE_EVENTS)(*hs)
+    _check(lib().chunkkv_compress_layers_hybrid(
+        prob.ref, ctypes.cast(ch, ctypes.c_void_p), n, n_reuse, ctypes.cast(qt, ctypes.c_void_p),
+        ctypes.cast(kt, ctypes.c_void_p), ctypes.cast(vt, ctypes.c_void_p), ctypes.cast(kot, ctypes.c_void_p),
+        ctypes.cast(vot, ctypes.c_void_p), _ptr(scores), _ptr(indices), _ptr(lengths), _ptr(workspace),
+        workspace_nbytes, _stream(stream), None if ev is None else ctypes.cast(ev, ctypes.c_void_p)))
+
+
+class HybridBuffers:
+    """Device outputs and workspace of one compress_layers_hybrid call
+    (layout from plan_hybrid), allocated with torch (memory plumbing only)."""
+
+    def __init__(self, prob: ProblemHandle, layer_chunk: Sequence[int], n_reuse: int, head_dim: int, dtype,
+                 device="cuda"):
+        import torch
+        hp = plan_hybrid(prob, layer_chunk, n_reuse)
+        self.hplan = hp
+        self.ws_bytes = hp["workspace_bytes"]
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.scores = torch.empty(hp["score_block_off"][-1], dtype=torch.float32, device=device)
+        self.indices = torch.empty(hp["index_block_off"][-1], dtype=torch.int32, device=device)
+        self.lengths = torch.empty(hp["length_block_off"][-1], dtype=torch.int32, device=device)
+        self.k_out = [torch.empty((r, head_dim), dtype=dtype, device=device) for r in hp["kv_out_rows"]]
+        self.v_out = [torch.empty((r, head_dim), dtype=dtype, device=device) for r in hp["kv_out_rows"]]
 
 
 class Buffers:

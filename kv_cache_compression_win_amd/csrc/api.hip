@@ -745,6 +745,94 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_dev[kMaxDevices] = {};
 
+// One run of consecutive layers that share a chunk size (the hybrid entry
+// points): its plan and where its anchors' blocks start in the caller's
+// scores / indices / lengths buffers.
+struct Run {
+  int l0 = 0, n = 0;
+  Plan pl;
+  int64_t score0 = 0, index0 = 0, length0 = 0;
+};
+
+// Splits the layers into runs of equal chunk size and plans each; n_anchor,
+// the block totals and the workspace the largest run needs.
+int plan_runs(const chunkkv_problem* p, const int32_t* layer_chunk, int n_layers, int n_reuse,
+              std::vector<Run>& runs, int& n_anchor, int64_t tot[3], size_t& ws) {
+  if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
+  if (!layer_chunk) return fail(CHUNKKV_ERR_INVALID_ARG, "layer_chunk is NULL");
+  if (n_layers < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "n_layers must be >= 1 (got %d)", n_layers);
+  if (n_reuse < 1) return fail(CHUNKKV_ERR_INVALID_ARG, "n_reuse must be >= 1 (got %d)", n_reuse);
+  runs.clear();
+  n_anchor = 0;
+  tot[0] = tot[1] = tot[2] = 0;
+  ws = 0;
+  for (int l = 0; l < n_layers;) {
+    int e = l + 1;
+    while (e < n_layers && layer_chunk[e] == layer_chunk[l]) ++e;
+    Run r;
+    r.l0 = l;
+    r.n = e - l;
+    chunkkv_problem q = *p;
+    q.chunk = layer_chunk[l];
+    const int rc = make_plan(&q, r.pl);
+    if (rc) return fail(rc, "layers %d-%d (chunk %d): %s", l, e - 1, layer_chunk[l], g_err.c_str());
+    r.score0 = tot[0];
+    r.index0 = tot[1];
+    r.length0 = tot[2];
+    const int na = (r.n + n_reuse - 1) / n_reuse;
+    n_anchor += na;
+    tot[0] += na * r.pl.scores_elems;
+    tot[1] += na * r.pl.index_elems;
+    tot[2] += na * r.pl.length_elems;
+    ws = std::max(ws, ws_need(r.pl, 1));
+    runs.push_back(std::move(r));
+    l = e;
+  }
+  return CHUNKKV_OK;
+}
+
+// Algorithm 2's scoring half over n_layers layers of one plan: the anchors'
+// scores and selections, as many anchors per launch as the workspace holds.
+hipError_t score_select_run(const Plan& pl, int n_layers, int n_reuse, const void* const* q_win,
+                            const void* const* k, float* scores, int32_t* indices, int32_t* lengths,
+                            void* workspace, size_t workspace_bytes, hipStream_t s) {
+  const int n_anchor = (n_layers + n_reuse - 1) / n_reuse;
+  int batch = std::min(n_anchor, kMaxLayers);
+  while (batch > 1 && ws_need(pl, batch) > workspace_bytes) --batch;
+  const XLayout xl = xlayout(pl, batch);
+  const Work w = carve(pl, batch, xl, workspace);
+  const void* qb[kMaxLayers];
+  const void* kb[kMaxLayers];
+  for (int a0 = 0; a0 < n_anchor; a0 += batch) {
+    const int na = std::min(batch, n_anchor - a0);
+    for (int i = 0; i < na; ++i) {
+      qb[i] = q_win[(a0 + i) * n_reuse];
+      kb[i] = k[(a0 + i) * n_reuse];
+    }
+    hipError_t e = run_scores(pl, xl, na, qb, kb, w, scores + a0 * pl.scores_elems, s);
+    if (e != hipSuccess) return e;
+    e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
+                   lengths + a0 * pl.length_elems, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Algorithm 2's gather half: layer l of the run copies its own K/V rows with
+// the indices of anchor floor(l / n_reuse).
+hipError_t gather_run(const Plan& pl, int n_layers, int n_reuse, const void* const* k, const void* const* v,
+                      void* const* ko, void* const* vo, const int32_t* indices, const int32_t* lengths,
+                      hipStream_t s) {
+  int32_t blocks[kMaxLayers];
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, n_layers - l0);
+    for (int i = 0; i < nl; ++i) blocks[i] = (l0 + i) / n_reuse;
+    const hipError_t e = run_gather(pl, nl, k + l0, v + l0, ko + l0, vo + l0, blocks, indices, lengths, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t static_scratch(float** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -963,6 +1051,81 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
   if (!gather_events && (e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+  return ok();
+}
+
+int chunkkv_plan_hybrid(const chunkkv_problem* p, const int32_t* layer_chunk, int32_t n_layers, int32_t n_reuse,
+                        int32_t* n_anchor, int64_t* score_block_off, int64_t* index_block_off,
+                        int64_t* length_block_off, int64_t* kv_out_rows, size_t* workspace_bytes) {
+  std::vector<Run> runs;
+  int na = 0;
+  int64_t tot[3];
+  size_t ws = 0;
+  const int rc = plan_runs(p, layer_chunk, n_layers, n_reuse, runs, na, tot, ws);
+  if (rc) return rc;
+  if (n_anchor) *n_anchor = na;
+  if (workspace_bytes) *workspace_bytes = ws;
+  int a = 0;
+  for (const Run& r : runs) {
+    for (int i = 0; i < (r.n + n_reuse - 1) / n_reuse; ++i, ++a) {
+      if (score_block_off) score_block_off[a] = r.score0 + i * r.pl.scores_elems;
+      if (index_block_off) index_block_off[a] = r.index0 + i * r.pl.index_elems;
+      if (length_block_off) length_block_off[a] = r.length0 + i * r.pl.length_elems;
+    }
+    if (kv_out_rows)
+      for (int l = r.l0; l < r.l0 + r.n; ++l) kv_out_rows[l] = r.pl.index_elems;
+  }
+  if (score_block_off) score_block_off[na] = tot[0];
+  if (index_block_off) index_block_off[na] = tot[1];
+  if (length_block_off) length_block_off[na] = tot[2];
+  return ok();
+}
+
+int chunkkv_compress_layers_hybrid(const chunkkv_problem* p, const int32_t* layer_chunk, int32_t n_layers,
+                                   int32_t n_reuse, const void* const* q_win, const void* const* k,
+                                   const void* const* v, void* const* k_out, void* const* v_out, float* scores,
+                                   int32_t* indices, int32_t* lengths, void* workspace, size_t workspace_bytes,
+                                   void* stream, void* const* phase_events) {
+  std::vector<Run> runs;
+  int na = 0;
+  int64_t tot[3];
+  size_t ws = 0;
+  int rc = plan_runs(p, layer_chunk, n_layers, n_reuse, runs, na, tot, ws);
+  if (rc) return rc;
+  if (!q_win || !k || !v || !k_out || !v_out)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "pointer tables must be non-NULL");
+  if (!scores || !indices || !lengths)
+    return fail(CHUNKKV_ERR_INVALID_ARG, "scores, indices and lengths must be non-NULL");
+  for (const Run& r : runs)
+    for (int l = r.l0; l < r.l0 + r.n; ++l) {
+      const bool anchor = (l - r.l0) % n_reuse == 0;
+      if (anchor && !q_win[l]) return fail(CHUNKKV_ERR_INVALID_ARG, "q_win[%d] is NULL on a scoring layer", l);
+      if (!k[l] || !v[l] || !k_out[l] || !v_out[l])
+        return fail(CHUNKKV_ERR_INVALID_ARG, "a K/V pointer of layer %d is NULL", l);
+      if ((anchor && !aligned16(q_win[l])) || !aligned16(k[l]) || !aligned16(v[l]) || !aligned16(k_out[l]) ||
+          !aligned16(v_out[l]))
+        return fail(CHUNKKV_ERR_UNSUPPORTED, "buffers of layer %d must be 16-byte aligned", l);
+    }
+  for (const Run& r : runs)
+    if ((rc = check_ws(r.pl, workspace, workspace_bytes, 1))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto record = [&](int i) -> hipError_t {
+    return phase_events && phase_events[i] ? hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s)
+                                           : hipSuccess;
+  };
+  hipError_t e = record(0);
+  if (e != hipSuccess) return hip_fail(e, "phase event");
+  for (const Run& r : runs)
+    if ((e = score_select_run(r.pl, r.n, n_reuse, q_win + r.l0, k + r.l0, scores + r.score0, indices + r.index0,
+                              lengths + r.length0, workspace, workspace_bytes, s)) != hipSuccess)
+      return hip_fail(e, "score / select launch");
+  if ((e = record(1)) != hipSuccess || (e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
+  for (const Run& r : runs)
+    if ((e = gather_run(r.pl, r.n, n_reuse, k + r.l0, v + r.l0, k_out + r.l0, v_out + r.l0, indices + r.index0,
+                        lengths + r.length0, s)) != hipSuccess)
+      return hip_fail(e, "gather launch");
+  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
   return ok();
 }
 

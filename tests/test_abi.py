@@ -169,3 +169,57 @@ def test_decode_attention_static_validates_before_launch():
     assert L.chunkkv_decode_attention_static(p.ref, None, dummy, dummy, dummy, dummy, None) == ck.ERR_INVALID_ARG
     assert L.chunkkv_decode_attention_static(p.ref, dummy, dummy + 2, dummy, dummy, dummy, None) == ck.ERR_UNSUPPORTED
     assert L.chunkkv_decode_attention_static(None, dummy, dummy, dummy, dummy, dummy, None) == ck.ERR_INVALID_ARG
+
+
+def test_plan_hybrid_blocks_follow_each_runs_plan():
+    # runs of equal chunk size (ChunkKV page, section 5.7, as a per-layer c):
+    # [0-2] c = 10, [3-4] c = 1, [5] c = 4; Algorithm 2 restarts at each run,
+    # so with n_reuse = 2 the anchors are layers 0, 2, 3 and 5
+    p = _p(seq_lens=[1000, 333], l_max=[100, 40])
+    chunks = [10, 10, 10, 1, 1, 4]
+    hp = ck.plan_hybrid(p, chunks, 2)
+    anchors = [0, 2, 3, 5]
+    assert hp["n_anchor"] == len(anchors)
+    per_c = {c: ck.plan(_p(seq_lens=[1000, 333], l_max=[100, 40], chunk=c)) for c in set(chunks)}
+    so = io = lo = 0
+    for a, l in enumerate(anchors):
+        assert (hp["score_block_off"][a], hp["index_block_off"][a], hp["length_block_off"][a]) == (so, io, lo)
+        pl = per_c[chunks[l]]
+        so, io, lo = so + pl["scores_elems"], io + pl["index_elems"], lo + pl["length_elems"]
+    assert (hp["score_block_off"][-1], hp["index_block_off"][-1], hp["length_block_off"][-1]) == (so, io, lo)
+    assert hp["kv_out_rows"] == [per_c[c]["index_elems"] for c in chunks]
+    assert hp["workspace_bytes"] == max(ck.workspace_bytes(_p(seq_lens=[1000, 333], l_max=[100, 40], chunk=c), 1)
+                                        for c in set(chunks))
+    # one chunk size for every layer: the blocks of chunkkv_compress_layers
+    one = ck.plan_hybrid(p, [10] * 5, 2)
+    pl = per_c[10]
+    assert one["n_anchor"] == 3
+    assert one["score_block_off"] == [a * pl["scores_elems"] for a in range(4)]
+    assert one["index_block_off"] == [a * pl["index_elems"] for a in range(4)]
+
+
+def test_hybrid_entry_points_validate_before_launch():
+    L = ck.lib()
+    p = _p()
+    with pytest.raises(ck.ChunkKVError) as e:
+        ck.plan_hybrid(p, [10, 10, 0, 0], 1)
+    assert e.value.status == ck.ERR_INVALID_ARG and "layers 2-3" in ck.last_error()
+    with pytest.raises(ck.ChunkKVError) as e:
+        ck.plan_hybrid(p, [10, 1], 0)
+    assert e.value.status == ck.ERR_INVALID_ARG
+    assert L.chunkkv_plan_hybrid(p.ref, None, 2, 1, None, None, None, None, None, None) == ck.ERR_INVALID_ARG
+    dummy = 1 << 20
+    chunks = (ctypes.c_int32 * 4)(10, 10, 10, 1)
+    P = ctypes.c_void_p * 4
+    full = P(dummy, dummy, dummy, dummy)
+    q_gap = P(dummy, None, dummy, None)      # layer 3 starts a run: it scores
+    q_ok = P(dummy, None, dummy, dummy)
+    tab = ctypes.cast(full, ctypes.c_void_p)
+
+    def call(q, ws_bytes):
+        return L.chunkkv_compress_layers_hybrid(p.ref, ctypes.cast(chunks, ctypes.c_void_p), 4, 2,
+                                                ctypes.cast(q, ctypes.c_void_p), tab, tab, tab, tab, dummy, dummy,
+                                                dummy, dummy, ws_bytes, None, None)
+
+    assert call(q_gap, 1 << 30) == ck.ERR_INVALID_ARG and "q_win[3]" in ck.last_error()
+    assert call(q_ok, 16) == ck.ERR_WORKSPACE
