@@ -253,8 +253,11 @@ int chunkkv_compress_layers(const chunkkv_problem *p, int32_t n_layers, int32_t 
  * chunkkv_sizes describes for the problem with that anchor's chunk size;
  * entry n_anchor of each array holds the buffer's total size in elements.
  * kv_out_rows[l] is the row count of layer l's K'/V' (the index_elems of its
- * chunk size).  workspace_bytes is the largest chunkkv_workspace_bytes(p_c, 1)
- * over the chunk sizes c used.
+ * chunk size).  workspace_bytes is the largest chunkkv_workspace_bytes(p_c,
+ * n_c) over the runs, n_c the run's anchor count: with it every run scores all
+ * its anchors (up to 32) in one launch per phase.  Any workspace of at least
+ * the largest chunkkv_workspace_bytes(p_c, 1) works, with fewer anchors per
+ * launch.
  *   n_anchor          HOST out, may be NULL
  *   *_block_off       HOST int64 [n_layers + 1] out (n_anchor <= n_layers),
  *                     each may be NULL
@@ -276,8 +279,9 @@ int chunkkv_plan_hybrid(const chunkkv_problem *p, const int32_t *layer_chunk, in
  *   scores, indices, lengths  DEVICE, the anchors' blocks at the offsets
  *                   chunkkv_plan_hybrid gives (totals in its entry n_anchor)
  *   k_out[l], v_out[l]  DEVICE, kv_out_rows[l] rows each
- *   workspace       DEVICE scratch of >= chunkkv_plan_hybrid's
- *                   workspace_bytes bytes
+ *   workspace       DEVICE scratch of >= the largest chunkkv_workspace_bytes
+ *                   (p_c, 1) over the chunk sizes used (chunkkv_plan_hybrid's
+ *                   workspace_bytes lets each run score all its anchors at once)
  *   phase_events    NULL, or HOST [CHUNKKV_N_PHASE_EVENTS] hipEvent_t
  *                   handles recorded on `stream` before the first scoring
  *                   launch, after the last selection (entries 1 and 2) and

@@ -755,7 +755,8 @@ struct Run {
 };
 
 // Splits the layers into runs of equal chunk size and plans each; n_anchor,
-// the block totals and the workspace the largest run needs.
+// the block totals and the workspace with which every run scores all its
+// anchors (at most kMaxLayers) in one launch per phase.
 int plan_runs(const chunkkv_problem* p, const int32_t* layer_chunk, int n_layers, int n_reuse,
               std::vector<Run>& runs, int& n_anchor, int64_t tot[3], size_t& ws) {
   if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
@@ -784,7 +785,7 @@ int plan_runs(const chunkkv_problem* p, const int32_t* layer_chunk, int n_layers
     tot[0] += na * r.pl.scores_elems;
     tot[1] += na * r.pl.index_elems;
     tot[2] += na * r.pl.length_elems;
-    ws = std::max(ws, ws_need(r.pl, 1));
+    ws = std::max(ws, ws_need(r.pl, std::min(na, kMaxLayers)));
     runs.push_back(std::move(r));
     l = e;
   }
