@@ -61,7 +61,10 @@ constexpr int kSharedKeySpans = 8;
 // scores) when a head has one row block: there the chunk partials U
 // (4*R_pad/c bytes per key token and head, written and read back) would
 // outweigh a second read of the keys (2*d bytes).
-constexpr int kTwoPassMaxChunk = 3;
+#ifndef CKV_TWO_PASS_MAX_CHUNK
+#define CKV_TWO_PASS_MAX_CHUNK 3
+#endif
+constexpr int kTwoPassMaxChunk = CKV_TWO_PASS_MAX_CHUNK;
 constexpr int kKSteps = kD / 16;     // MFMA k-steps per logit tile
 // LDS of an exchange-mode workgroup at most (three per 160 KB CU) and the
 // share of it kept for the launch tables.
