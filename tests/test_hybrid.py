@@ -65,12 +65,9 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype,seq_lens,l_max,Hq,Hkv,d,w,chunks,n_reuse", CASES)
-def test_hybrid_matches_oracle_per_run(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse):
-    L = len(chunks)
-    q, k, v = _inputs(dtype, seq_lens, L, Hq, Hkv, d, w, seed=len(chunks) + sum(seq_lens))
-    prob = ck.make_problem(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks[0])
-    hb = _hybrid(prob, chunks, n_reuse, q, k, v, d, tdtype(dtype))
+def _check_oracle(hb, dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse, q, k, v):
+    """Every anchor's scores and selection and every layer's gathered rows of
+    a hybrid call against the oracle's Algorithm 2 on each run of layers."""
     hp = hb.hplan
     scores, indices, lengths = hb.scores.cpu().numpy(), hb.indices.cpu().numpy(), hb.lengths.cpu().numpy()
     starts = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int64)
@@ -108,6 +105,52 @@ def test_hybrid_matches_oracle_per_run(dtype, seq_lens, l_max, Hq, Hkv, d, w, ch
                         assert np.all(got[n:].view(np.uint8) == POISON_BYTE), where
         anchor += -(-(e - l0) // n_reuse)
     assert anchor == hp["n_anchor"]
+
+
+@pytest.mark.parametrize("dtype,seq_lens,l_max,Hq,Hkv,d,w,chunks,n_reuse", CASES)
+def test_hybrid_matches_oracle_per_run(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse):
+    L = len(chunks)
+    q, k, v = _inputs(dtype, seq_lens, L, Hq, Hkv, d, w, seed=len(chunks) + sum(seq_lens))
+    prob = ck.make_problem(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks[0])
+    hb = _hybrid(prob, chunks, n_reuse, q, k, v, d, tdtype(dtype))
+    _check_oracle(hb, dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse, q, k, v)
+
+
+def test_hybrid_graph_replays_match_eager():
+    # the hybrid call allocates nothing and issues only kernel launches, so it
+    # can be captured in a HIP graph; every replay (eager poison fills and
+    # synchronisations between them) reproduces the eager outputs, which are
+    # themselves checked against the oracle
+    dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse = CASES[1]
+    L = len(chunks)
+    dt = tdtype(dtype)
+    q, k, v = _inputs(dtype, seq_lens, L, Hq, Hkv, d, w, seed=11)
+    prob = ck.make_problem(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks[0])
+    ref = _hybrid(prob, chunks, n_reuse, q, k, v, d, dt)
+    _check_oracle(ref, dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse, q, k, v)
+    hb = ck.HybridBuffers(prob, chunks, n_reuse, d, dt)
+    qs = [q[l] for l in range(L)]
+    stream = torch.cuda.Stream()
+    args = (prob, chunks, n_reuse, qs, [k[l] for l in range(L)], [v[l] for l in range(L)], hb.k_out, hb.v_out,
+            hb.scores, hb.indices, hb.lengths, hb.workspace, hb.ws_bytes)
+    with torch.cuda.stream(stream):
+        ck.compress_layers_hybrid(*args, stream=stream)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        ck.compress_layers_hybrid(*args, stream=stream)
+    torch.cuda.synchronize()
+    outs = [hb.scores, hb.indices, hb.lengths] + hb.k_out + hb.v_out
+    refs = [ref.scores, ref.indices, ref.lengths] + ref.k_out + ref.v_out
+    for rep in range(3):
+        for t in [hb.scores, hb.lengths] + hb.k_out + hb.v_out:
+            t.view(torch.uint8).fill_(POISON_BYTE)
+        hb.indices.fill_(POISON_INDEX)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, refs)):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (rep, i)
 
 
 @pytest.mark.parametrize("dtype,seq_lens,l_max,Hq,Hkv,d,w,chunks,n_reuse", CASES[:2])
