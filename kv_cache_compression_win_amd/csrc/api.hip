@@ -792,16 +792,31 @@ int plan_runs(const chunkkv_problem* p, const int32_t* layer_chunk, int n_layers
   return CHUNKKV_OK;
 }
 
+// Records phase event i (if any) on stream s.
+hipError_t record_event(void* const* events, int i, hipStream_t s) {
+  return events && events[i] ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+}
+
 // Algorithm 2's scoring half over n_layers layers of one plan: the anchors'
 // scores and selections, as many anchors per launch as the workspace holds.
+// Phase events 0 and 1 (events may be NULL) bracket the scoring: a scoring
+// phase that is one launch of the MFMA score kernel takes them at that
+// kernel's own start and end; otherwise they are recorded between kernels
+// (entry 1 after the first batch's scores when there is one batch, after the
+// last selection when there are several).
 hipError_t score_select_run(const Plan& pl, int n_layers, int n_reuse, const void* const* q_win,
                             const void* const* k, float* scores, int32_t* indices, int32_t* lengths,
-                            void* workspace, size_t workspace_bytes, hipStream_t s) {
+                            void* workspace, size_t workspace_bytes, hipStream_t s, void* const* events) {
   const int n_anchor = (n_layers + n_reuse - 1) / n_reuse;
   int batch = std::min(n_anchor, kMaxLayers);
   while (batch > 1 && ws_need(pl, batch) > workspace_bytes) --batch;
-  const XLayout xl = xlayout(pl, batch);
+  const XLayout xl = xlayout(pl, batch);   // the last, shorter launch keeps this span layout
   const Work w = carve(pl, batch, xl, workspace);
+  const bool one_batch = n_anchor <= batch;
+  const bool score_events = events && one_batch && pl.mfma && !pl.two_pass && pl.B <= kMaxSeqs;
+  auto ev = [&](int i) { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
+  hipError_t e = score_events ? hipSuccess : record_event(events, 0, s);
+  if (e != hipSuccess) return e;
   const void* qb[kMaxLayers];
   const void* kb[kMaxLayers];
   for (int a0 = 0; a0 < n_anchor; a0 += batch) {
@@ -810,28 +825,38 @@ hipError_t score_select_run(const Plan& pl, int n_layers, int n_reuse, const voi
       qb[i] = q_win[(a0 + i) * n_reuse];
       kb[i] = k[(a0 + i) * n_reuse];
     }
-    hipError_t e = run_scores(pl, xl, na, qb, kb, w, scores + a0 * pl.scores_elems, s);
+    float* sc = scores + a0 * pl.scores_elems;
+    // the score phase: the exchange kernel, or chunk partials and their
+    // combine, or the two passes over the keys
+    e = score_events ? run_scores(pl, xl, na, qb, kb, w, sc, s, ev(0), ev(1)) : run_scores(pl, xl, na, qb, kb, w, sc, s);
     if (e != hipSuccess) return e;
-    e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
-                   lengths + a0 * pl.length_elems, s);
+    if (one_batch && !score_events && (e = record_event(events, 1, s)) != hipSuccess) return e;
+    e = run_select(pl, na, sc, indices + a0 * pl.index_elems, lengths + a0 * pl.length_elems, s);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return one_batch ? hipSuccess : record_event(events, 1, s);
 }
 
 // Algorithm 2's gather half: layer l of the run copies its own K/V rows with
-// the indices of anchor floor(l / n_reuse).
+// the indices of anchor floor(l / n_reuse).  Phase events 2 and 3 (events may
+// be NULL) bracket it, at the kernel's own start and end when the gather is
+// one launch.
 hipError_t gather_run(const Plan& pl, int n_layers, int n_reuse, const void* const* k, const void* const* v,
                       void* const* ko, void* const* vo, const int32_t* indices, const int32_t* lengths,
-                      hipStream_t s) {
+                      hipStream_t s, void* const* events) {
+  const bool gather_events = events && n_layers <= kMaxLayers && pl.B <= kMaxSeqs;
+  auto ev = [&](int i) { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
+  hipError_t e = gather_events ? hipSuccess : record_event(events, 2, s);
+  if (e != hipSuccess) return e;
   int32_t blocks[kMaxLayers];
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, n_layers - l0);
     for (int i = 0; i < nl; ++i) blocks[i] = (l0 + i) / n_reuse;
-    const hipError_t e = run_gather(pl, nl, k + l0, v + l0, ko + l0, vo + l0, blocks, indices, lengths, s);
+    e = gather_events ? run_gather(pl, nl, k + l0, v + l0, ko + l0, vo + l0, blocks, indices, lengths, s, ev(2), ev(3))
+                      : run_gather(pl, nl, k + l0, v + l0, ko + l0, vo + l0, blocks, indices, lengths, s);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return gather_events ? hipSuccess : record_event(events, 3, s);
 }
 
 hipError_t static_scratch(float** out) {
@@ -1002,56 +1027,13 @@ int chunkkv_compress_layers(const chunkkv_problem* p, int32_t n_layers, int32_t 
         !aligned16(k_out[l]) || !aligned16(v_out[l]))
       return fail(CHUNKKV_ERR_UNSUPPORTED, "buffers of layer %d must be 16-byte aligned", l);
   }
-  const int n_anchor = (n_layers + n_reuse - 1) / n_reuse;
   if ((rc = check_ws(pl, workspace, workspace_bytes, 1))) return rc;
-  int batch = std::min(n_anchor, kMaxLayers);
-  while (batch > 1 && ws_need(pl, batch) > workspace_bytes) --batch;
-  const XLayout xl = xlayout(pl, batch);   // the last, shorter launch keeps this span layout
-
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto ev = [&](int i) { return phase_events ? static_cast<hipEvent_t>(phase_events[i]) : nullptr; };
-  auto record = [&](int i) -> hipError_t { return ev(i) ? hipEventRecord(ev(i), s) : hipSuccess; };
-  const bool one_batch = n_anchor <= batch;
-  // a phase that is one kernel launch takes its events at that kernel's start
-  // and end (no separate stream markers between the kernels of a step)
-  const bool score_events = one_batch && pl.mfma && !pl.two_pass && pl.B <= kMaxSeqs;
-  const bool gather_events = n_layers <= kMaxLayers && pl.B <= kMaxSeqs;
-  hipError_t e = score_events ? hipSuccess : record(0);
-  if (e != hipSuccess) return hip_fail(e, "phase event");
-
-  const Work w = carve(pl, batch, xl, workspace);
-  const void* qb[kMaxLayers];
-  const void* kb[kMaxLayers];
-  for (int a0 = 0; a0 < n_anchor; a0 += batch) {
-    const int na = std::min(batch, n_anchor - a0);
-    for (int i = 0; i < na; ++i) {
-      qb[i] = q_win[(a0 + i) * n_reuse];
-      kb[i] = k[(a0 + i) * n_reuse];
-    }
-    float* sc = scores + a0 * pl.scores_elems;
-    // the score phase: the exchange kernel, or chunk partials and their
-    // combine, or the two passes over the keys
-    if ((e = score_events ? run_scores(pl, xl, na, qb, kb, w, sc, s, ev(0), ev(1))
-                          : run_scores(pl, xl, na, qb, kb, w, sc, s)) != hipSuccess)
-      return hip_fail(e, "score launch");
-    if (one_batch && !score_events && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-    if ((e = run_select(pl, na, scores + a0 * pl.scores_elems, indices + a0 * pl.index_elems,
-                        lengths + a0 * pl.length_elems, s)) != hipSuccess)
-      return hip_fail(e, "select launch");
-  }
-  if (!one_batch && (e = record(1)) != hipSuccess) return hip_fail(e, "phase event");
-  if (!gather_events && (e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
-
-  int32_t blocks[kMaxLayers];
-  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
-    const int nl = std::min(kMaxLayers, n_layers - l0);
-    for (int i = 0; i < nl; ++i) blocks[i] = (l0 + i) / n_reuse;
-    e = gather_events ? run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s,
-                                   ev(2), ev(3))
-                      : run_gather(pl, nl, k + l0, v + l0, k_out + l0, v_out + l0, blocks, indices, lengths, s);
-    if (e != hipSuccess) return hip_fail(e, "gather launch");
-  }
-  if (!gather_events && (e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+  hipError_t e = score_select_run(pl, n_layers, n_reuse, q_win, k, scores, indices, lengths, workspace,
+                                  workspace_bytes, s, phase_events);
+  if (e != hipSuccess) return hip_fail(e, "score / select launch");
+  if ((e = gather_run(pl, n_layers, n_reuse, k, v, k_out, v_out, indices, lengths, s, phase_events)) != hipSuccess)
+    return hip_fail(e, "gather launch");
   return ok();
 }
 
@@ -1111,22 +1093,19 @@ int chunkkv_compress_layers_hybrid(const chunkkv_problem* p, const int32_t* laye
     if ((rc = check_ws(r.pl, workspace, workspace_bytes, 1))) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto record = [&](int i) -> hipError_t {
-    return phase_events && phase_events[i] ? hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s)
-                                           : hipSuccess;
-  };
-  hipError_t e = record(0);
+  hipError_t e = record_event(phase_events, 0, s);
   if (e != hipSuccess) return hip_fail(e, "phase event");
   for (const Run& r : runs)
     if ((e = score_select_run(r.pl, r.n, n_reuse, q_win + r.l0, k + r.l0, scores + r.score0, indices + r.index0,
-                              lengths + r.length0, workspace, workspace_bytes, s)) != hipSuccess)
+                              lengths + r.length0, workspace, workspace_bytes, s, nullptr)) != hipSuccess)
       return hip_fail(e, "score / select launch");
-  if ((e = record(1)) != hipSuccess || (e = record(2)) != hipSuccess) return hip_fail(e, "phase event");
+  if ((e = record_event(phase_events, 1, s)) != hipSuccess || (e = record_event(phase_events, 2, s)) != hipSuccess)
+    return hip_fail(e, "phase event");
   for (const Run& r : runs)
     if ((e = gather_run(r.pl, r.n, n_reuse, k + r.l0, v + r.l0, k_out + r.l0, v_out + r.l0, indices + r.index0,
-                        lengths + r.length0, s)) != hipSuccess)
+                        lengths + r.length0, s, nullptr)) != hipSuccess)
       return hip_fail(e, "gather launch");
-  if ((e = record(3)) != hipSuccess) return hip_fail(e, "phase event");
+  if ((e = record_event(phase_events, 3, s)) != hipSuccess) return hip_fail(e, "phase event");
   return ok();
 }
 
