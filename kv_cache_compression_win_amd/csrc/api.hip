@@ -92,6 +92,9 @@ int exchange_spin_limit() {
   return x < 0 ? 0 : (x > (1 << 24) ? (1 << 24) : static_cast<int>(x));
 }
 
+// Score work items per layer that keep a single-layer launch's CUs busy.
+constexpr int64_t kMinLayerItems = 192;
+
 int make_plan(const chunkkv_problem* p, Plan& pl) {
   if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
   if (p->reserved != 0) return fail(CHUNKKV_ERR_INVALID_ARG, "reserved field must be 0");
@@ -148,6 +151,39 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   pl.x_max_span = pl.mfma && pl.n_rb == 1 && !pl.two_pass && !exchange_disabled()
                       ? score_exchange_max_span_chunks(pl.c) : 0;
   pl.u_packed = pl.dtype == CHUNKKV_BF16;
+  // A layer with few score work items at the full span (one short sequence:
+  // 8 KV heads x 14 spans of an 8k-token layer at c = 10) leaves most CUs
+  // idle in a single-layer call, and each span's chain of dependent key
+  // groups sets the launch's length: such layers take shorter spans, in whole
+  // MFMA groups and at least half the full span, until a layer has
+  // kMinLayerItems items.  Measured per single-layer call: 8k tokens at c = 10
+  // and 16k at c = 20 (112 items at 60-chunk spans) 30.7 and 33.9 us with
+  // 30-chunk spans against 33.9 and 39.1 us; 16k at c = 10 (224 items) is
+  // fastest at the full span (36.3 us; 39-41 us with 30-48-chunk spans).  The
+  // two-pass final mode keeps the full span (its LDS row sums are laid out
+  // for it).
+  if (pl.mfma && !pl.two_pass) {
+    auto layer_items = [&](int span) {
+      int64_t n = 0;
+      for (int b = 0; b < pl.B; ++b) {
+        const int64_t C = std::max<int64_t>(0, p->seq_start[b + 1] - p->seq_start[b] + pl.c - 1) / pl.c;
+        n += static_cast<int64_t>(pl.Hkv) * pl.n_rb * ((C + span - 1) / span);
+      }
+      return n;
+    };
+    const int floor_span = std::max(pl.group_chunks, pl.span_chunks / 2 / pl.group_chunks * pl.group_chunks);
+    int span = pl.span_chunks;
+    while (span - pl.group_chunks >= floor_span && layer_items(span) < kMinLayerItems) span -= pl.group_chunks;
+    pl.span_chunks = span;
+  }
+#ifdef CKV_SPAN_ENV
+  if (pl.mfma && !pl.two_pass)
+    if (const char* v = std::getenv("CHUNKKV_SCORE_SPAN")) {
+      const int sp = std::atoi(v);
+      if (sp >= pl.group_chunks && sp <= score_mfma_span_chunks(pl.c) && sp % pl.group_chunks == 0)
+        pl.span_chunks = sp;
+    }
+#endif
   pl.kv_st = p->kv_stride_tok;
   pl.kv_sh = p->kv_stride_head;
   pl.q_ss = p->q_stride_seq;
