@@ -429,10 +429,9 @@ constexpr int64_t kCombineMinBlocks = 512;
 constexpr int64_t kFuseLseBytes = 32768;
 
 // lse_only: the row statistics alone (the two-pass path's final pass reads them).
-hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
-                       hipStream_t s, bool lse_only = false) {
-  // spans per combine block: fewer when the launch would otherwise have too
-  // few blocks to spread over the GPU (a layer or two of short sequences)
+// Spans per combine block: fewer when the launch would otherwise have too
+// few blocks to spread over the GPU (a layer or two of short sequences).
+int combine_spb(const Plan& pl, int nl) {
   int spb = combine_spans_per_blk(pl.R_pad);
   auto n_blocks = [&](int per) {
     int64_t n = 0;
@@ -440,54 +439,68 @@ hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st,
     return n * nl;
   };
   while (spb > 1 && n_blocks(spb) < kCombineMinBlocks) spb /= 2;
+  return spb;
+}
+
+// Combine (and row-statistics) parameters of nl scoring layers of sequences
+// [b0, b0 + nb), spb spans per block.
+CombineParams combine_params(const Plan& pl, int nl, int b0, int nb, int spb, const float* U, const float2* st,
+                             float2* lse, float* scores, bool lse_only) {
+  CombineParams P{};
+  P.n_layers = nl;
+  P.n_seqs = nb;
+  P.span_chunks = pl.span_chunks;
+  P.spans_per_blk = spb;
+  int items = 0;
+  for (int i = 0; i < nb; ++i) {
+    const Seq& sq = pl.seq[b0 + i];
+    P.C[i] = sq.C;
+    P.n_span[i] = sq.n_span;
+    P.n_blk[i] = (sq.n_span + spb - 1) / spb;
+    P.item0[i] = items;
+    P.u_off[i] = sq.u_off;
+    P.st_off[i] = sq.st_off;
+    P.score_off[i] = sq.score_off;
+    P.lse_off[i] = sq.lse_off;
+    P.head0[i] = i * pl.Hkv;
+    items += pl.Hkv * P.n_blk[i];
+  }
+  P.item0[nb] = items;
+  P.head0[nb] = nb * pl.Hkv;
+  P.items_per_layer = items;
+  P.u_layer_stride = pl.u_elems;
+  P.st_layer_stride = pl.st_elems;
+  P.score_layer_stride = pl.scores_elems;
+  P.lse_layer_stride = pl.lse_elems;
+  P.U = U;
+  P.u_packed = pl.u_packed ? 1 : 0;
+  P.stats = st;
+  P.lse = lse;
+  P.scores = scores;
+  P.H_kv = pl.Hkv;
+  P.R = pl.R;
+  P.R_pad = pl.R_pad;
+  P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
+  // short heads (span statistics of at most kFuseLseBytes, one round of
+  // loads at 128 rows): every combine block forms its head's row statistics
+  // itself, which saves a launch (8k layer: 38 -> 35 us per call); with
+  // more spans the repeated reads cost more than the launch (32k layers)
+  int64_t st_bytes = 0;
+  for (int i = 0; i < nb; ++i) st_bytes = std::max<int64_t>(st_bytes, int64_t{8} * P.n_span[i] * pl.R_pad);
+  P.fuse_lse = st_bytes <= kFuseLseBytes && !lse_only ? 1 : 0;
+  return P;
+}
+
+hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
+                       hipStream_t s, bool lse_only = false) {
+  const int spb = combine_spb(pl, nl);
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
-    CombineParams P{};
-    P.n_layers = nl;
-    P.n_seqs = nb;
-    P.span_chunks = pl.span_chunks;
-    P.spans_per_blk = spb;
-    int items = 0;
-    for (int i = 0; i < nb; ++i) {
-      const Seq& sq = pl.seq[b0 + i];
-      P.C[i] = sq.C;
-      P.n_span[i] = sq.n_span;
-      P.n_blk[i] = (sq.n_span + spb - 1) / spb;
-      P.item0[i] = items;
-      P.u_off[i] = sq.u_off;
-      P.st_off[i] = sq.st_off;
-      P.score_off[i] = sq.score_off;
-      P.lse_off[i] = sq.lse_off;
-      P.head0[i] = i * pl.Hkv;
-      items += pl.Hkv * P.n_blk[i];
-    }
-    P.item0[nb] = items;
-    P.head0[nb] = nb * pl.Hkv;
-    P.items_per_layer = items;
-    P.u_layer_stride = pl.u_elems;
-    P.st_layer_stride = pl.st_elems;
-    P.score_layer_stride = pl.scores_elems;
-    P.lse_layer_stride = pl.lse_elems;
-    P.U = U;
-    P.u_packed = pl.u_packed ? 1 : 0;
-    P.stats = st;
-    P.lse = lse;
-    P.scores = scores;
-    P.H_kv = pl.Hkv;
-    P.R = pl.R;
-    P.R_pad = pl.R_pad;
-    P.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(pl.d)));
-    // short heads (span statistics of at most kFuseLseBytes, one round of
-    // loads at 128 rows): every combine block forms its head's row statistics
-    // itself, which saves a launch (8k layer: 38 -> 35 us per call); with
-    // more spans the repeated reads cost more than the launch (32k layers)
-    int64_t st_bytes = 0;
-    for (int i = 0; i < nb; ++i) st_bytes = std::max<int64_t>(st_bytes, int64_t{8} * P.n_span[i] * pl.R_pad);
-    P.fuse_lse = st_bytes <= kFuseLseBytes && !lse_only ? 1 : 0;
+    const CombineParams P = combine_params(pl, nl, b0, nb, spb, U, st, lse, scores, lse_only);
     hipError_t e = P.fuse_lse ? hipSuccess : launch_row_lse(P, nl * nb * pl.Hkv, s);
     if (e != hipSuccess) return e;
     if (lse_only) continue;
-    e = launch_combine(P, nl * items, s);
+    e = launch_combine(P, nl * P.items_per_layer, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -618,36 +631,82 @@ hipError_t run_scores(const Plan& pl, const XLayout& xl, int nl, const void* con
   return run_score(pl, nl, q, k, w.U, w.st, s, nullptr, nullptr, kScoreFinal, w.lse, scores);
 }
 
+// Selection parameters of nl scoring layers of sequences [b0, b0 + nb).
+SelectParams select_params(const Plan& pl, int nl, int b0, int nb, const float* scores, int32_t* indices,
+                           int32_t* lengths) {
+  SelectParams P{};
+  P.n_layers = nl;
+  P.n_seqs = nb;
+  P.H_kv = pl.Hkv;
+  P.w = pl.w;
+  P.c = pl.c;
+  for (int i = 0; i < nb; ++i) {
+    const Seq& sq = pl.seq[b0 + i];
+    P.T[i] = sq.T;
+    P.C[i] = sq.C;
+    P.kk[i] = sq.kk;
+    P.L_cap[i] = sq.L_cap;
+    P.len_off[i] = (b0 + i) * pl.Hkv;
+    P.score_off[i] = sq.score_off;
+    P.index_off[i] = sq.index_off;
+  }
+  P.score_layer_stride = pl.scores_elems;
+  P.index_layer_stride = pl.index_elems;
+  P.len_layer_stride = pl.length_elems;
+  P.scores = scores;
+  P.indices = indices;
+  P.lengths = lengths;
+  return P;
+}
+
 hipError_t run_select(const Plan& pl, int nl, const float* scores, int32_t* indices, int32_t* lengths,
                       hipStream_t s) {
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
-    SelectParams P{};
-    P.n_layers = nl;
-    P.n_seqs = nb;
-    P.H_kv = pl.Hkv;
-    P.w = pl.w;
-    P.c = pl.c;
-    for (int i = 0; i < nb; ++i) {
-      const Seq& sq = pl.seq[b0 + i];
-      P.T[i] = sq.T;
-      P.C[i] = sq.C;
-      P.kk[i] = sq.kk;
-      P.L_cap[i] = sq.L_cap;
-      P.len_off[i] = (b0 + i) * pl.Hkv;
-      P.score_off[i] = sq.score_off;
-      P.index_off[i] = sq.index_off;
-    }
-    P.score_layer_stride = pl.scores_elems;
-    P.index_layer_stride = pl.index_elems;
-    P.len_layer_stride = pl.length_elems;
-    P.scores = scores;
-    P.indices = indices;
-    P.lengths = lengths;
-    const hipError_t e = launch_select(P, nl * nb * pl.Hkv, s);
+    const hipError_t e = launch_select(select_params(pl, nl, b0, nb, scores, indices, lengths), nl * nb * pl.Hkv, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Gather parameters of nl layers of sequences [b0, b0 + nb); layer i reads
+// index block blocks[i].
+GatherParams gather_params(const Plan& pl, int nl, const void* const* k, const void* const* v, void* const* ko,
+                           void* const* vo, const int32_t* blocks, const int32_t* indices, const int32_t* lengths,
+                           int b0, int nb) {
+  GatherParams P{};
+  for (int i = 0; i < nl; ++i) {
+    P.k[i] = k[i];
+    P.v[i] = v[i];
+    P.ko[i] = ko[i];
+    P.vo[i] = vo[i];
+    P.idx_block[i] = blocks[i];
+  }
+  P.n_layers = nl;
+  P.n_seqs = nb;
+  P.H_kv = pl.Hkv;
+  int items = 0;
+  for (int i = 0; i < nb; ++i) {
+    const Seq& sq = pl.seq[b0 + i];
+    P.tok0[i] = sq.tok0;
+    P.T[i] = sq.T;
+    P.L_cap[i] = sq.L_cap;
+    P.len_off[i] = (b0 + i) * pl.Hkv;
+    P.item0[i] = items;
+    P.blocks_per_head[i] = (sq.L_cap + kGatherRows - 1) / kGatherRows;
+    P.index_off[i] = sq.index_off;
+    items += pl.Hkv * P.blocks_per_head[i];
+  }
+  P.item0[nb] = items;
+  P.items_per_layer = items;
+  P.index_layer_stride = pl.index_elems;
+  P.len_layer_stride = pl.length_elems;
+  P.indices = indices;
+  P.lengths = lengths;
+  P.row_bytes = pl.d * pl.eb;
+  P.kv_st_bytes = pl.kv_st * pl.eb;
+  P.kv_sh_bytes = pl.kv_sh * pl.eb;
+  return P;
 }
 
 // Gathers layers [l0, l0 + nl); layer l reads index block blocks[l - l0].
@@ -657,39 +716,8 @@ hipError_t run_gather(const Plan& pl, int nl, const void* const* k, const void* 
                       hipEvent_t ev_stop = nullptr) {
   for (int b0 = 0; b0 < pl.B; b0 += kMaxSeqs) {
     const int nb = std::min(kMaxSeqs, pl.B - b0);
-    GatherParams P{};
-    for (int i = 0; i < nl; ++i) {
-      P.k[i] = k[i];
-      P.v[i] = v[i];
-      P.ko[i] = ko[i];
-      P.vo[i] = vo[i];
-      P.idx_block[i] = blocks[i];
-    }
-    P.n_layers = nl;
-    P.n_seqs = nb;
-    P.H_kv = pl.Hkv;
-    int items = 0;
-    for (int i = 0; i < nb; ++i) {
-      const Seq& sq = pl.seq[b0 + i];
-      P.tok0[i] = sq.tok0;
-      P.T[i] = sq.T;
-      P.L_cap[i] = sq.L_cap;
-      P.len_off[i] = (b0 + i) * pl.Hkv;
-      P.item0[i] = items;
-      P.blocks_per_head[i] = (sq.L_cap + kGatherRows - 1) / kGatherRows;
-      P.index_off[i] = sq.index_off;
-      items += pl.Hkv * P.blocks_per_head[i];
-    }
-    P.item0[nb] = items;
-    P.items_per_layer = items;
-    P.index_layer_stride = pl.index_elems;
-    P.len_layer_stride = pl.length_elems;
-    P.indices = indices;
-    P.lengths = lengths;
-    P.row_bytes = pl.d * pl.eb;
-    P.kv_st_bytes = pl.kv_st * pl.eb;
-    P.kv_sh_bytes = pl.kv_sh * pl.eb;
-    const hipError_t e = launch_gather(P, nl * items, s, ev_start, ev_stop);
+    const GatherParams P = gather_params(pl, nl, k, v, ko, vo, blocks, indices, lengths, b0, nb);
+    const hipError_t e = launch_gather(P, nl * P.items_per_layer, s, ev_start, ev_stop);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -313,7 +313,7 @@ __global__ __launch_bounds__(NTH) void select_fast_kernel(const SelectParams P) 
   int n_ge = C;
   int buf = 0;
   auto wg_sum = [&](int4 v) {
-    red[buf][wave] = v;
+    if ((tid & 63) == 0) red[buf][wave] = v;   // v is uniform across the wave
     __syncthreads();
     int4 t = red[buf][0];
 #pragma unroll
