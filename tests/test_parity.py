@@ -417,11 +417,13 @@ def test_llama3_8b_32layer_T32768_all_units():
 
 
 def test_chunk_size_sweep_T16384():
+    # every chunk size and budget of the sweep, every KV head against the
+    # oracle (the scores of a 16384-token head cost about 0.7 s of host time)
     wl = kvsynth.WORKLOADS["llama3-8b-csweep-T16384"]
     cache = kvsynth.make_cache(wl, device="cuda", seed=0)
     refs = {}
     for c in kvsynth.CSWEEP_CHUNKS:
-        for h in (0, 5):
+        for h in range(wl.n_kv_heads):
             refs[(c, h)] = POOL.submit(oracle.chunk_scores, kvsynth.host_array(cache["q_win"][0, 0]),
                                        kvsynth.host_array(cache["k"][0]), h, wl.n_q_heads, wl.window, c)
     for c in kvsynth.CSWEEP_CHUNKS:
@@ -429,7 +431,7 @@ def test_chunk_size_sweep_T16384():
             case = Case(ck.BF16, wl.seq_lens, (l_max,), wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                         wl.window, c, 1, cache["q_win"], cache["k"], cache["v"]).run()
             _props_all_units(case)
-            for h in (0, 5):
+            for h in range(wl.n_kv_heads):
                 check_unit(case, 0, 0, h, s_ref=refs[(c, h)].result())
 
 
@@ -443,10 +445,12 @@ def test_llama70b_batch_sampled():
                 wl.chunk, wl.n_reuse, cache["q_win"], cache["k"], cache["v"]).run()
     _props_all_units(case)
     _gather_all_layers_on_gpu(case)
-    # the oracle on every head of the 16384-token sequence and on sampled
-    # heads of the others (a 131072-token unit costs about 20 s of host time)
-    units = [(a, 3, h) for a in (0, 2) for h in range(case.Hkv)]
-    units += [(0, 2, 3), (2, 2, 6), (0, 1, 1), (2, 0, 5)]
+    # the oracle on every head of the 32768- and 16384-token sequences and on
+    # two heads of each longer one, for both scoring layers (a 131072-token
+    # unit costs about 20 s of host time; about 260 s in all, spread over
+    # the host's threads)
+    units = [(a, b, h) for a in (0, 2) for b in (2, 3) for h in range(case.Hkv)]
+    units += [(a, b, h) for a in (0, 2) for b, hs in ((0, (5, 2)), (1, (1, 6))) for h in hs]
     jobs = {(a, b, h): POOL.submit(oracle.chunk_scores, case.host_q(a, b), case.host_kv(case.k, a, b),
                                    h, case.Hq, case.w, case.c) for (a, b, h) in units}
     for (a, b, h), fut in jobs.items():
