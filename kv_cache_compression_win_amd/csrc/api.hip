@@ -426,9 +426,13 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
 // spans per block are reduced.
 constexpr int64_t kCombineMinBlocks = 512;
 
-constexpr int64_t kFuseLseBytes = 32768;
+// Heads whose span statistics take at most this many bytes have every
+// combine block form the row statistics itself (no row-statistics launch).
+#ifndef CKV_FUSE_LSE_BYTES
+#define CKV_FUSE_LSE_BYTES 32768
+#endif
+constexpr int64_t kFuseLseBytes = CKV_FUSE_LSE_BYTES;
 
-// lse_only: the row statistics alone (the two-pass path's final pass reads them).
 // Spans per combine block: fewer when the launch would otherwise have too
 // few blocks to spread over the GPU (a layer or two of short sequences).
 int combine_spb(const Plan& pl, int nl) {
@@ -491,6 +495,7 @@ CombineParams combine_params(const Plan& pl, int nl, int b0, int nb, int spb, co
   return P;
 }
 
+// lse_only: the row statistics alone (the two-pass path's final pass reads them).
 hipError_t run_combine(const Plan& pl, int nl, const float* U, const float2* st, float2* lse, float* scores,
                        hipStream_t s, bool lse_only = false) {
   const int spb = combine_spb(pl, nl);
