@@ -176,14 +176,6 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     while (span - pl.group_chunks >= floor_span && layer_items(span) < kMinLayerItems) span -= pl.group_chunks;
     pl.span_chunks = span;
   }
-#ifdef CKV_SPAN_ENV
-  if (pl.mfma && !pl.two_pass)
-    if (const char* v = std::getenv("CHUNKKV_SCORE_SPAN")) {
-      const int sp = std::atoi(v);
-      if (sp >= pl.group_chunks && sp <= score_mfma_span_chunks(pl.c) && sp % pl.group_chunks == 0)
-        pl.span_chunks = sp;
-    }
-#endif
   pl.kv_st = p->kv_stride_tok;
   pl.kv_sh = p->kv_stride_head;
   pl.q_ss = p->q_stride_seq;
