@@ -337,9 +337,13 @@ def cpu_baseline(wl, cache, n_pairs: int):
             "host": {"cpu_model": model, "logical_cpus": os.cpu_count()}}
 
 
-def layer_latency_context(name, args, start, stop, chunk=None, l_max=None, calls=40, blocks=5):
+def layer_latency_context(name, args, start, stop, chunk=None, l_max=None, calls=40, blocks=5, copies=16):
     """A single-layer compress_layers call (score, select and gather of one
-    layer): median and minimum over blocks of back-to-back calls."""
+    layer): median and minimum over blocks of back-to-back calls, once on the
+    same input (which the 256 MB last-level cache may partly hold between
+    calls) and once rotating over `copies` copies of the input in distinct
+    memory (together larger than that cache), so that every call reads its
+    keys and kept rows from HBM."""
     import torch
     import kvsynth
     from kv_cache_compression_win_amd import chunkkv as ck
@@ -350,23 +354,35 @@ def layer_latency_context(name, args, start, stop, chunk=None, l_max=None, calls
     prob = ck.make_problem(ck.BF16, wl.seq_lens, lm, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, c)
     bufs = ck.Buffers(prob, 1, 1, wl.head_dim, torch.bfloat16, "cuda")
 
-    def call():
-        ck.compress_layers(prob, 1, [cache["q_win"][0]], [cache["k"][0]], [cache["v"][0]], [bufs.k_out[0]],
-                           [bufs.v_out[0]], bufs.scores, bufs.indices, bufs.lengths, bufs.workspace, bufs.ws_bytes)
+    inputs = [(cache["q_win"][0], cache["k"][0], cache["v"][0])]
+    inputs += [tuple(x.clone() for x in inputs[0]) for _ in range(copies - 1)]
 
-    for _ in range(args.warmup):
-        call()
+    def call(i):
+        q, k, v = inputs[i]
+        ck.compress_layers(prob, 1, [q], [k], [v], [bufs.k_out[0]], [bufs.v_out[0]], bufs.scores, bufs.indices,
+                           bufs.lengths, bufs.workspace, bufs.ws_bytes)
+
+    def timed(rotate):
+        us = []
+        for _ in range(blocks):
+            start.record()
+            for j in range(calls):
+                call(j % copies if rotate else 0)
+            stop.record()
+            torch.cuda.synchronize()
+            us.append(start.elapsed_time(stop) / calls * 1e3)
+        return us
+
+    for j in range(max(args.warmup, copies)):
+        call(j % copies)
     torch.cuda.synchronize()
-    us = []
-    for _ in range(blocks):
-        start.record()
-        for _ in range(calls):
-            call()
-        stop.record()
-        torch.cuda.synchronize()
-        us.append(start.elapsed_time(stop) / calls * 1e3)
-    return {"workload": name, "chunk": c, "l_max": list(lm), "us_per_call_median": statistics.median(us),
-            "us_per_call_min": min(us), "blocks": blocks, "calls_per_block": calls}
+    same = timed(False)
+    rot = timed(True)
+    in_bytes = sum(x.numel() * x.element_size() for x in inputs[0])
+    return {"workload": name, "chunk": c, "l_max": list(lm), "us_per_call_median": statistics.median(same),
+            "us_per_call_min": min(same), "blocks": blocks, "calls_per_block": calls,
+            "rotated_inputs": {"copies": copies, "input_mb_per_copy": round(in_bytes / 2**20, 1),
+                               "us_per_call_median": statistics.median(rot), "us_per_call_min": min(rot)}}
 
 
 def context_70b(args):
