@@ -25,10 +25,14 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned HIP device memory.  The library never
- *     allocates, frees or keeps device memory.  Host pointers (problem
+ *     allocates, frees or keeps device memory (the one exception is the fixed
+ *     scratch array inside the library that chunkkv_decode_attention_static
+ *     uses instead of a workspace).  Host pointers (problem
  *     struct and the arrays it points to, pointer tables) are read during the
  *     call only.  All buffers must stay valid until the work queued on
- *     `stream` (a hipStream_t; NULL = default stream) has finished.
+ *     `stream` (a hipStream_t; NULL = default stream) has finished.  Streams
+ *     and events are passed as void pointers so that this header needs no
+ *     HIP header: plain C callers and foreign-function bindings use it as is.
  *   - Arguments are validated on the host before anything is launched.  A
  *     non-OK status means nothing was launched and nothing was written;
  *     chunkkv_last_error() then returns a message (thread-local).
@@ -89,7 +93,7 @@ typedef struct {
   int32_t head_dim;          /* d: 8..256, d * elem_bytes multiple of 16 */
   int32_t window;            /* w >= 1 */
   int32_t chunk;             /* c >= 1 */
-  int32_t reserved;          /* must be 0 */
+  int32_t reserved;          /* must be 0 (keeps the 64-bit fields aligned; room for a flag) */
   int64_t kv_stride_tok, kv_stride_head;
   int64_t q_stride_seq, q_stride_row, q_stride_head;
 } chunkkv_problem;
@@ -175,6 +179,8 @@ int chunkkv_score(const chunkkv_problem *p, const void *q_win, const void *k, fl
  *            and every index lies in [0, T_b).
  *   indices  DEVICE int32 out, index_elems entries (entries i >= n untouched)
  *   lengths  DEVICE int32 out, length_elems entries
+ * No workspace: a head's scores are held in registers (C_b <= 32768) or
+ * re-read from `scores`.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
 int chunkkv_select(const chunkkv_problem *p, const float *scores, int32_t *indices,
