@@ -62,6 +62,10 @@ CASES = [
     (ck.BF16, [700, 333], [140, 70], 8, 2, 128, 16, [10, 10, 10, 10, 1, 1, 1, 1], 2),
     (ck.BF16, [900], [300], 8, 2, 128, 16, [10, 10, 4, 1, 1, 10], 2),
     (ck.F32, [500, 64], [100, 30], 4, 2, 64, 8, [8, 8, 8, 1, 1], 3),
+    # more anchors in one run than one launch scores (36 > 32) and more
+    # sequences than one launch holds (9 > 8), every layer an anchor
+    (ck.BF16, [300, 200, 257, 128, 199, 310, 64, 96, 150], [60, 40, 51, 25, 39, 62, 12, 19, 30], 8, 2, 128, 16,
+     [10] * 36 + [1] * 4, 1),
 ]
 
 
@@ -153,7 +157,7 @@ def test_hybrid_graph_replays_match_eager():
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (rep, i)
 
 
-@pytest.mark.parametrize("dtype,seq_lens,l_max,Hq,Hkv,d,w,chunks,n_reuse", CASES[:2])
+@pytest.mark.parametrize("dtype,seq_lens,l_max,Hq,Hkv,d,w,chunks,n_reuse", CASES[:2] + CASES[3:])
 def test_hybrid_equals_one_call_per_run(dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse):
     L = len(chunks)
     dt = tdtype(dtype)
