@@ -369,3 +369,18 @@ class Buffers:
         self.lengths = torch.empty(self.n_anchor * pl["length_elems"], dtype=torch.int32, device=device)
         self.k_out = torch.empty((n_layers, pl["index_elems"], head_dim), dtype=dtype, device=device)
         self.v_out = torch.empty((n_layers, pl["index_elems"], head_dim), dtype=dtype, device=device)
+        self.n_reuse = n_reuse
+        self.n_kv_heads = prob.struct.n_kv_heads
+
+    def kept(self, layer: int, seq: int, head: int):
+        """(K' rows, V' rows, kept token positions) of KV head `head` of
+        sequence `seq` in layer `layer` after a compress_layers call into these
+        buffers: views of the outputs, n rows each, n being the head's length
+        of the layer's anchor (read from the device, so this synchronises)."""
+        pl = self.plan
+        a = layer // self.n_reuse
+        cap = pl["l_cap"][seq]
+        n = int(self.lengths[a * pl["length_elems"] + seq * self.n_kv_heads + head])
+        r0 = pl["index_off"][seq] + head * cap
+        i0 = a * pl["index_elems"] + r0
+        return self.k_out[layer, r0:r0 + n], self.v_out[layer, r0:r0 + n], self.indices[i0:i0 + n]

@@ -41,3 +41,7 @@ def test_readme_example_runs_and_layout_holds():
             idx = indices[a * per_anchor + h * l_cap: a * per_anchor + h * l_cap + n].long().to("cuda")
             assert torch.equal(buf.k_out[l][h * l_cap: h * l_cap + n], k[l][idx, h])
             assert torch.equal(buf.v_out[l][h * l_cap: h * l_cap + n], v[l][idx, h])
+            kk, vv, pos = buf.kept(l, 0, h)
+            assert torch.equal(pos.long(), idx) and torch.equal(kk, k[l][idx, h]) and torch.equal(vv, v[l][idx, h])
+    kk, vv, pos = ns["k_kept"], ns["v_kept"], ns["positions"]
+    assert kk.shape[0] == vv.shape[0] == pos.numel() > 0
