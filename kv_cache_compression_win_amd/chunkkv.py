@@ -349,6 +349,36 @@ class HybridBuffers:
         self.lengths = torch.empty(hp["length_block_off"][-1], dtype=torch.int32, device=device)
         self.k_out = [torch.empty((r, head_dim), dtype=dtype, device=device) for r in hp["kv_out_rows"]]
         self.v_out = [torch.empty((r, head_dim), dtype=dtype, device=device) for r in hp["kv_out_rows"]]
+        self.n_reuse = n_reuse
+        self.n_kv_heads = prob.struct.n_kv_heads
+        # runs of equal chunk size: (first layer, end, first anchor, that chunk size's plan)
+        self.runs = []
+        l, a = 0, 0
+        while l < len(layer_chunk):
+            e = l
+            while e < len(layer_chunk) and layer_chunk[e] == layer_chunk[l]:
+                e += 1
+            st = Problem.from_buffer_copy(prob.struct)
+            st.chunk = int(layer_chunk[l])
+            self.runs.append((l, e, a, plan(ProblemHandle(st, prob.seq_start, prob.l_max))))
+            a += -(-(e - l) // n_reuse)
+            l = e
+
+    def kept(self, layer: int, seq: int, head: int):
+        """As Buffers.kept, for a compress_layers_hybrid call into these
+        buffers: the layer's run gives its chunk size, anchor and offsets."""
+        for l0, e, a0, pl in self.runs:
+            if l0 <= layer < e:
+                break
+        else:
+            raise IndexError(f"layer {layer} outside the plan")
+        hp = self.hplan
+        a = a0 + (layer - l0) // self.n_reuse
+        cap = pl["l_cap"][seq]
+        n = int(self.lengths[hp["length_block_off"][a] + seq * self.n_kv_heads + head])
+        r0 = pl["index_off"][seq] + head * cap
+        i0 = hp["index_block_off"][a] + r0
+        return self.k_out[layer][r0:r0 + n], self.v_out[layer][r0:r0 + n], self.indices[i0:i0 + n]
 
 
 class Buffers:

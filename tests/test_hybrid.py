@@ -100,8 +100,14 @@ def _check_oracle(hb, dtype, seq_lens, l_max, Hq, Hkv, d, w, chunks, n_reuse, q,
                         check_scores(s_gpu, s_ref, dtype, where)
                         check_selection(s_gpu, s_ref, idx, T, w, c, l_max[b] // c, dtype, where)
                         assert np.all(indices[io + n:io + cap] == POISON_INDEX), where
+                    # the binding's view of the same head
+                    kk, vv, pos = hb.kept(l, b, h)
+                    assert np.array_equal(pos.cpu().numpy(), idx), where
                     # gathered rows: this layer's own K/V at the anchor's indices
                     ro = pl["index_off"][b] + h * cap
+                    assert kk.shape[0] == vv.shape[0] == n, where
+                    assert kk.data_ptr() == hb.k_out[l][ro:].data_ptr(), where
+                    assert vv.data_ptr() == hb.v_out[l][ro:].data_ptr(), where
                     for t, name in ((hb.k_out[l], "k"), (hb.v_out[l], "v")):
                         got = kvsynth.host_array(t[ro:ro + cap])
                         src = ks[i] if name == "k" else vs[i]
