@@ -72,6 +72,7 @@ def test_bf16_mfma_chunk_sizes(c):
     (ck.BF16, 128, 7, 4, 1, 32),     # chunk size without a static layout
     (ck.BF16, 128, 100, 4, 2, 8),    # chunk size beyond the MFMA layouts
     (ck.F32, 32, 3, 2, 2, 4),
+    (ck.F32, 64, 10, 64, 1, 64),     # G*w = 4096 rows, the largest supported (3-chunk spans)
 ])
 def test_generic_path(dtype, d, c, Hq, Hkv, w):
     case = random_case(dtype, [1201], [300], Hq, Hkv, d, w, c, seed=d + c).run()
@@ -84,6 +85,7 @@ def test_generic_path(dtype, d, c, Hq, Hkv, w):
     (64, 8, 64, 5), (64, 8, 64, 20),                  # 4 row blocks, 1 and 4 tiles per group
     (16, 2, 32, 10), (16, 2, 32, 5),                  # 2 row blocks, 2 KV heads
     (32, 4, 48, 10),                                  # 3 row blocks
+    (64, 1, 64, 10), (32, 2, 256, 10),                # G*w = 4096, the largest supported: 32 row blocks
 ])
 def test_mfma_row_blocks(Hq, Hkv, w, c):
     # G*w not a multiple of 32 (padding rows), and G*w > 128 (several row
