@@ -212,6 +212,41 @@ def paged_context(wl, cache, prob, bufs, args, start, stop, page_rows=256):
             "hbm_gbps": {"paged": nbytes / (us_p * 1e-6) / 1e9, "contiguous": nbytes / (us_c * 1e-6) / 1e9}}
 
 
+def reuse_context(wl, cache, prob, args, start, stop, reuse=(1, 2, 4)):
+    """Layer-wise index reuse (ChunkKV page, section 4.2, Algorithm 2): the
+    same stack compressed with N_reuse = 1 (every layer scores), 2 and 4, one
+    chunkkv_compress_layers call per step, so the cost that reuse removes is
+    measured directly."""
+    import torch
+    from kv_cache_compression_win_amd import chunkkv as ck
+    L = wl.n_layers
+    ks, vs = [cache["k"][l] for l in range(L)], [cache["v"][l] for l in range(L)]
+    out = {}
+    for nr in reuse:
+        b = ck.Buffers(prob, L, nr, wl.head_dim, torch.bfloat16, "cuda")
+        qs = [cache["q_win"][l] if l % nr == 0 else None for l in range(L)]
+
+        def call():
+            ck.compress_layers(prob, nr, qs, ks, vs, [b.k_out[l] for l in range(L)],
+                               [b.v_out[l] for l in range(L)], b.scores, b.indices, b.lengths, b.workspace,
+                               b.ws_bytes)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            call()
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        out[f"n_reuse_{nr}"] = {"scoring_layers": -(-L // nr), "ms_per_step": ms,
+                                "value": L * sum(wl.seq_lens) / (ms * 1e-3), "unit": "layer-tokens/s"}
+        del b
+        torch.cuda.empty_cache()
+    return out
+
+
 def hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args, start, stop):
     """The hybrid layer policy (ChunkKV page, section 5.7): the lower half of
     the layers keeps chunk size c, the upper half scores single tokens (c = 1,
@@ -631,6 +666,8 @@ def main():
     if args.context == "on" and L >= 4 and wl.chunk > 1:
         extra["hybrid_policy"] = hybrid_policy(wl, prob, bufs, qs, ks, vs, kos, vos, n_reuse, args,
                                                start, stop)
+    if args.context == "on" and L >= 4:
+        extra["index_reuse"] = reuse_context(wl, cache, prob, args, start, stop)
     n_copy = 1 << 30 if args.context == "on" else 0
     if n_copy:
         extra["copy_peak"] = copy_peak(n_copy, start, stop, step_gbps)
