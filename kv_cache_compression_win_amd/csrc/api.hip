@@ -56,12 +56,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Seq {
   int64_t tok0;
   int32_t T, C, kk, L_cap, n_span;
+  int32_t n_span_final;   // two passes: spans of the final pass (n_span counts the statistics pass's)
   int64_t score_off, index_off, u_off, st_off, lse_off;
 };
 
 struct Plan {
   int dtype = 0, eb = 0, B = 0, Hq = 0, Hkv = 0, G = 0, d = 0, w = 0, c = 0;
   int R = 0, R_pad = 0, n_rb = 0, span_chunks = 0;
+  int final_span = 0;      // two passes: the final pass's span (its LDS layout's); span_chunks is the statistics pass's
   bool mfma = false;
   bool two_pass = false;   // statistics pass + final-score pass, no chunk partials
   bool u_packed = false;   // chunk partials stored in 24 bits (bf16 problems)
@@ -94,6 +96,13 @@ int exchange_spin_limit() {
 
 // Score work items per layer that keep a single-layer launch's CUs busy.
 constexpr int64_t kMinLayerItems = 192;
+
+// Longest span of the statistics pass of two-pass plans, in final-pass spans
+// (a power of two).
+#ifndef CKV_STATS_SPAN_MAX
+#define CKV_STATS_SPAN_MAX 16
+#endif
+constexpr int kStatsSpanMax = CKV_STATS_SPAN_MAX;
 
 int make_plan(const chunkkv_problem* p, Plan& pl) {
   if (!p) return fail(CHUNKKV_ERR_INVALID_ARG, "problem is NULL");
@@ -147,10 +156,32 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   // per key token and head, written and read back) would outweigh a second
   // pass over the keys (2*d bytes)
   pl.two_pass = pl.mfma && pl.n_rb == 1 && score_two_pass_supported(pl.c);
+  pl.final_span = pl.span_chunks;
   pl.group_chunks = pl.mfma ? score_group_chunks(pl.c) : 0;
   pl.x_max_span = pl.mfma && pl.n_rb == 1 && !pl.two_pass && !exchange_disabled()
                       ? score_exchange_max_span_chunks(pl.c) : 0;
   pl.u_packed = pl.dtype == CHUNKKV_BF16;
+  auto layer_items = [&](int64_t span) {
+    int64_t n = 0;
+    for (int b = 0; b < pl.B; ++b) {
+      const int64_t C = std::max<int64_t>(0, p->seq_start[b + 1] - p->seq_start[b] + pl.c - 1) / pl.c;
+      n += static_cast<int64_t>(pl.Hkv) * pl.n_rb * ((C + span - 1) / span);
+    }
+    return n;
+  };
+  // Two passes: the statistics pass keeps no chunk partials in LDS, so its
+  // spans may be several final-pass spans long (fewer span starts, whose
+  // first group forms the row maximum, and fewer span statistics), while a
+  // layer keeps kMinLayerItems items; the final pass keeps the span its LDS
+  // row sums are laid out for.  Measured per call (final spans x 1 / 4 / 8 /
+  // 16): 16k tokens at c = 1 98.7 / 86.5 / 86.5 / 95 us, c = 2 62.5 / 57.9 /
+  // 65.3 / 81.7, c = 3 60.1 / 60.2 / 71.5 / 95; the 32-layer 32k stack at
+  // c = 1 (16 scoring layers) 908-916 / 831 / 803-813 / 795-812 us per step.
+  if (pl.two_pass) {
+    int f = kStatsSpanMax;
+    while (f > 1 && layer_items(static_cast<int64_t>(pl.final_span) * f) < kMinLayerItems) f /= 2;
+    pl.span_chunks = pl.final_span * f;
+  }
   // A layer with few score work items at the full span (one short sequence:
   // 8 KV heads x 14 spans of an 8k-token layer at c = 10) leaves most CUs
   // idle in a single-layer call, and each span's chain of dependent key
@@ -159,18 +190,8 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
   // kMinLayerItems items.  Measured per single-layer call: 8k tokens at c = 10
   // and 16k at c = 20 (112 items at 60-chunk spans) 30.7 and 33.9 us with
   // 30-chunk spans against 33.9 and 39.1 us; 16k at c = 10 (224 items) is
-  // fastest at the full span (36.3 us; 39-41 us with 30-48-chunk spans).  The
-  // two-pass final mode keeps the full span (its LDS row sums are laid out
-  // for it).
+  // fastest at the full span (36.3 us; 39-41 us with 30-48-chunk spans).
   if (pl.mfma && !pl.two_pass) {
-    auto layer_items = [&](int span) {
-      int64_t n = 0;
-      for (int b = 0; b < pl.B; ++b) {
-        const int64_t C = std::max<int64_t>(0, p->seq_start[b + 1] - p->seq_start[b] + pl.c - 1) / pl.c;
-        n += static_cast<int64_t>(pl.Hkv) * pl.n_rb * ((C + span - 1) / span);
-      }
-      return n;
-    };
     const int floor_span = std::max(pl.group_chunks, pl.span_chunks / 2 / pl.group_chunks * pl.group_chunks);
     int span = pl.span_chunks;
     while (span - pl.group_chunks >= floor_span && layer_items(span) < kMinLayerItems) span -= pl.group_chunks;
@@ -199,6 +220,7 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     s.kk = static_cast<int32_t>(std::min<int64_t>(p->l_max[b] / pl.c, s.C));
     s.L_cap = static_cast<int32_t>(std::min<int64_t>(T, static_cast<int64_t>(s.kk) * pl.c + pl.w));
     s.n_span = (s.C + pl.span_chunks - 1) / pl.span_chunks;
+    s.n_span_final = (s.C + pl.final_span - 1) / pl.final_span;
     s.score_off = pl.scores_elems;
     s.index_off = pl.index_elems;
     s.u_off = pl.u_elems;
@@ -209,7 +231,7 @@ int make_plan(const chunkkv_problem* p, Plan& pl) {
     if (!pl.two_pass) pl.u_elems += static_cast<int64_t>(pl.Hkv) * s.C * u_row_words(pl.R_pad, pl.u_packed);
     pl.st_elems += static_cast<int64_t>(pl.Hkv) * s.n_span * pl.R_pad;
     pl.lse_elems += static_cast<int64_t>(pl.Hkv) * pl.R_pad;
-    items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * s.n_span;
+    items += static_cast<int64_t>(pl.Hkv) * pl.n_rb * std::max(s.n_span, s.n_span_final);
     pl.seq.push_back(s);
   }
   if (items * kMaxLayers > 2000000000LL)
@@ -362,7 +384,8 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
     }
     P.n_layers = nl;
     P.n_seqs = nb;
-    P.span_chunks = pl.span_chunks;
+    const bool final_pass = mode == kScoreFinal;
+    P.span_chunks = final_pass ? pl.final_span : pl.span_chunks;
     int items = 0;
     for (int i = 0; i < nb; ++i) {
       const Seq& sq = pl.seq[b0 + i];
@@ -370,13 +393,13 @@ hipError_t run_score(const Plan& pl, int nl, const void* const* q, const void* c
       P.qseq[i] = b0 + i;
       P.T[i] = sq.T;
       P.C[i] = sq.C;
-      P.n_span[i] = sq.n_span;
+      P.n_span[i] = final_pass ? sq.n_span_final : sq.n_span;
       P.item0[i] = items;
       P.u_off[i] = sq.u_off;
       P.st_off[i] = sq.st_off;
       P.s_off[i] = sq.score_off;
       P.lse_off[i] = sq.lse_off;
-      items += pl.Hkv * pl.n_rb * sq.n_span;
+      items += pl.Hkv * pl.n_rb * P.n_span[i];
     }
     P.item0[nb] = items;
     P.items_per_layer = items;

@@ -160,11 +160,18 @@ __device__ __forceinline__ void group_softmax(f32x16 (&acc)[Geo<CC>::NT], bool f
       }
   }
   float u[G::CPH];
-  bool ok = true;
+  // a span's first group (m_ref still -inf) needs the group maximum anyway:
+  // its exponentials are only formed once, against that maximum
+  bool ok = __builtin_amdgcn_readfirstlane(gi) != 0;
+  if (ok) {
 #pragma unroll
-  for (int q = 0; q < G::CPH; ++q) {
-    u[q] = chunk_exp_sum<CC>(acc, q, scale, -m_ref * scale);
-    ok = ok && (u[q] < 0x1p63f);   // false for +inf and NaN too
+    for (int q = 0; q < G::CPH; ++q) {
+      u[q] = chunk_exp_sum<CC>(acc, q, scale, -m_ref * scale);
+      ok = ok && (u[q] < 0x1p63f);   // false for +inf and NaN too
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < G::CPH; ++q) u[q] = 0.0f;
   }
   if (__ballot(!ok) != 0) {
     float mx = -INFINITY;
